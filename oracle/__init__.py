@@ -1,0 +1,141 @@
+"""CPU oracle for the affine-Q4 row-batched GEMV -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package. It shares no code with the device library ``affine_q4_gemv_amd`` and
+never imports it.
+
+* :func:`gemv` / :func:`gemv_rows` -- the plain definition, in double precision, from
+  ``q4ref.c`` (C, pthreads). Codes are taken unpacked (u8 per code).
+* :func:`prepare_x` -- what the activation prep produces: the f16 even/odd streams and the
+  per-32-chunk sums of the same f16-rounded values. Follows the Constant BATCH_MSL page,
+  quantized_rows consumers and the ``fn_norm_prep_b`` / ``fn_moe_act_b`` kernels: element
+  ``2k`` goes to ``xe[k]``, element ``2k+1`` to ``xo[k]``, and each 32-element chunk
+  contributes one sum. The sum is taken over the f16-rounded values, as ``fn_moe_act_b``
+  does (``fn_norm_prep_b`` sums the f32 values instead; the f16 reading keeps the bias term
+  and the code term on the same x).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4ref.c")
+_LIB = os.path.join(_HERE, "libq4ref.so")
+_lib = None
+
+GROUP = 64
+
+
+def build(force: bool = True) -> str:
+    """Compile ``q4ref.c`` into ``oracle/libq4ref.so`` with the host C compiler."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared", "-pthread",
+                        _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.q4ref_gemv.argtypes = [p, p, p, p, i64, i64, i64, i64, p, p, ctypes.c_int]
+        lib.q4ref_gemv.restype = ctypes.c_int
+        lib.q4ref_gemv_rows.argtypes = [p, p, p, p, i64, i64, i64, i64, p, p, i64, p, p,
+                                        ctypes.c_int]
+        lib.q4ref_gemv_rows.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _check(codes, scales, biases, x):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if codes.ndim != 3 or x.ndim != 3:
+        raise ValueError("codes [n_mat][out][in] and x [n_mat][nb][in] expected")
+    n_mat, out_dim, in_dim = codes.shape
+    if in_dim % GROUP or scales.shape != (n_mat, out_dim, in_dim // GROUP) \
+            or biases.shape != scales.shape or x.shape[0] != n_mat or x.shape[2] != in_dim:
+        raise ValueError("inconsistent shapes")
+    if codes.size and codes.max() > 15:
+        raise ValueError("codes must be 0..15")
+    return codes, scales, biases, x
+
+
+def gemv(codes, scales, biases, x, nthreads: int | None = None, with_bound: bool = True):
+    """y[m][r][o] (f64 [n_mat][nb][out]) and the per-element bound sum_i |Sqx|+|Bx|."""
+    codes, scales, biases, x = _check(codes, scales, biases, x)
+    n_mat, out_dim, in_dim = codes.shape
+    nb = x.shape[1]
+    y = np.empty((n_mat, nb, out_dim), dtype=np.float64)
+    bound = np.empty_like(y) if with_bound else None
+    rc = _load().q4ref_gemv(codes.ctypes.data, scales.ctypes.data, biases.ctypes.data,
+                            x.ctypes.data, n_mat, out_dim, in_dim, nb, y.ctypes.data,
+                            bound.ctypes.data if with_bound else None,
+                            nthreads or default_threads())
+    if rc:
+        raise ValueError(f"q4ref_gemv returned {rc}")
+    return y, bound
+
+
+def gemv_rows(codes, scales, biases, x, mats, rows, nthreads: int | None = None):
+    """Selected outputs: for each (mats[t], rows[t]) all nb values -> y, bound [n_sel][nb]."""
+    codes, scales, biases, x = _check(codes, scales, biases, x)
+    n_mat, out_dim, in_dim = codes.shape
+    nb = x.shape[1]
+    mats = np.ascontiguousarray(mats, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if mats.shape != rows.shape or mats.ndim != 1:
+        raise ValueError("mats and rows must be 1-D of equal length")
+    y = np.empty((mats.size, nb), dtype=np.float64)
+    bound = np.empty_like(y)
+    rc = _load().q4ref_gemv_rows(codes.ctypes.data, scales.ctypes.data, biases.ctypes.data,
+                                 x.ctypes.data, n_mat, out_dim, in_dim, nb, mats.ctypes.data,
+                                 rows.ctypes.data, mats.size, y.ctypes.data,
+                                 bound.ctypes.data, nthreads or default_threads())
+    if rc:
+        raise ValueError(f"q4ref_gemv_rows returned {rc}")
+    return y, bound
+
+
+def prepare_x(x):
+    """Activation prep: x f32 [n][in] -> (xe, xo) f16 [n][in/2] and xsum f64 [n][in/32].
+
+    f32 -> f16 is IEEE round-to-nearest-even (numpy's conversion); xsum[n][c] is the exact
+    sum (in double) of the 32 f16-rounded values of chunk c."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] % 32:
+        raise ValueError("x must be [n_rows][in_dim] with in_dim % 32 == 0")
+    with np.errstate(over="ignore"):  # |x| > 65504 -> inf, as IEEE conversion does
+        xh = x.astype(np.float16)
+    xe = np.ascontiguousarray(xh[:, 0::2])
+    xo = np.ascontiguousarray(xh[:, 1::2])
+    xsum = xh.astype(np.float64).reshape(x.shape[0], x.shape[1] // 32, 32).sum(axis=2)
+    return xe, xo, xsum
+
+
+def xsum_error_bound(x):
+    """Bound on |f32 sum - exact sum| for each 32-chunk of f16 values summed in f32 in any
+    order: 31 * 2^-24 * sum |x_i| (standard recursive-summation bound, 31 additions)."""
+    with np.errstate(over="ignore"):
+        xh = np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)
+    a = np.abs(xh).reshape(xh.shape[0], xh.shape[1] // 32, 32).sum(axis=2)
+    return 31.0 * 2.0 ** -24 * a

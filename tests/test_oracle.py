@@ -1,0 +1,323 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: a dense double matvec built with a
+different bf16 decoder (torch's), exact rational arithmetic, closed forms whose value is known
+before anything is computed, one-hot layout probes and invariants. Each pin is written so that
+a plausible mistake in the oracle (a dropped or sign-flipped term, a wrong scale/bias/x/code
+index, a wrong bf16 decode) fails at least one of them; ``test_mutants_are_caught`` plants
+such mistakes in copies of the oracle source and checks exactly that.
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ONE_BF16 = 0x3F80  # bf16 bits of 1.0
+
+
+def bf16_torch(bits):
+    """Independent bf16 decode: reinterpret through torch's bfloat16 dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).double().numpy()
+
+
+def pow2_bf16(e):
+    """bf16 bits of 2**e (exact)."""
+    return np.uint16(((int(e) + 127) & 0xFF) << 7)
+
+
+def dense_reference(codes, scales, biases, x):
+    """Dequantise to a dense double W and multiply with numpy: y [m][nb][out]."""
+    s = bf16_torch(scales)
+    b = bf16_torch(biases)
+    w = s.repeat(64, axis=2) * codes.astype(np.float64) + b.repeat(64, axis=2)
+    xd = x.astype(np.float64)
+    y = np.matmul(xd, np.transpose(w, (0, 2, 1)))
+    bound = np.matmul(np.abs(xd), np.transpose(np.abs(s.repeat(64, axis=2) * codes)
+                                               + np.abs(b.repeat(64, axis=2)), (0, 2, 1)))
+    return y, bound
+
+
+# --------------------------------------------------------------------------------------
+# the pin battery, parameterised by the gemv under test (so mutants can be run through it)
+
+def _case(n_mat, out_dim, in_dim, nb, seed):
+    c = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=seed)
+    return c["codes"], c["scales"], c["biases"], c["x"]
+
+
+def pin_bruteforce(gemv):
+    for (m, o, i, nb, seed) in [(1, 1, 64, 1, 1), (2, 3, 128, 2, 2), (1, 8, 192, 3, 3),
+                                (2, 5, 320, 2, 4)]:
+        q, s, b, x = _case(m, o, i, nb, seed)
+        y, bound = gemv(q, s, b, x)
+        yr, br = dense_reference(q, s, b, x)
+        if not np.all(np.abs(y - yr) <= 1e-12 * br + 1e-300):
+            return False
+        if not np.allclose(bound, br, rtol=1e-12, atol=0):
+            return False
+    return True
+
+
+def pin_zero_at_midcode(gemv):
+    """codes == 8 and B = -8 S  =>  W == 0, so y == 0 exactly for any x and any S."""
+    q, s, b, x = _case(2, 7, 256, 3, 5)
+    q[:] = 8
+    y, _ = gemv(q, s, b, x)
+    return bool(np.all(y == 0.0))
+
+
+def pin_row_sum(gemv):
+    """S = 1, B = 0, x = 1  =>  y = sum of the row's codes (an integer)."""
+    q, s, b, x = _case(2, 9, 320, 2, 6)
+    s[:] = ONE_BF16
+    b[:] = 0
+    x[:] = 1.0
+    y, _ = gemv(q, s, b, x)
+    want = q.astype(np.int64).sum(axis=2)  # [m][out]
+    return bool(np.all(y == want[:, None, :]))
+
+
+def pin_one_hot(gemv):
+    """A single code 1 at (m, o, i), S = 1, B = 0, distinct exact x: y[m][r][o] = x[m][r][i]."""
+    rng = np.random.default_rng(7)
+    n_mat, out_dim, in_dim, nb = 3, 5, 192, 3
+    x = (np.arange(n_mat * nb * in_dim, dtype=np.float32) + 1).reshape(n_mat, nb, in_dim)
+    for _ in range(6):
+        m, o, i = rng.integers(n_mat), rng.integers(out_dim), rng.integers(in_dim)
+        q = np.zeros((n_mat, out_dim, in_dim), np.uint8)
+        q[m, o, i] = 1
+        s = np.full((n_mat, out_dim, in_dim // 64), ONE_BF16, np.uint16)
+        b = np.zeros_like(s)
+        y, _ = gemv(q, s, b, x)
+        want = np.zeros((n_mat, nb, out_dim))
+        want[m, :, o] = x[m, :, i]
+        if not np.array_equal(y, want):
+            return False
+    return True
+
+
+def pin_scale_position(gemv):
+    """q = 1, B = 0, S[m][o][g] = 2^(g + 3o + 7m), x = 1 on group g0 only: y = 64 S[m][o][g0]."""
+    n_mat, out_dim, in_dim, nb = 2, 4, 384, 2
+    g = in_dim // 64
+    e = (np.arange(g)[None, None, :] + 3 * np.arange(out_dim)[None, :, None]
+         + 7 * np.arange(n_mat)[:, None, None])
+    s = np.vectorize(pow2_bf16)(e - 20).astype(np.uint16)
+    q = np.ones((n_mat, out_dim, in_dim), np.uint8)
+    b = np.zeros_like(s)
+    for g0 in range(g):
+        x = np.zeros((n_mat, nb, in_dim), np.float32)
+        x[:, :, 64 * g0:64 * g0 + 64] = 1.0
+        y, _ = gemv(q, s, b, x)
+        want = 64.0 * np.exp2(e[:, :, g0] - 20.0)
+        if not np.array_equal(y, np.broadcast_to(want[:, None, :], y.shape)):
+            return False
+    return True
+
+
+def pin_bias_position(gemv):
+    """q = 0, B[m][o][g] = 2^(g + 3o + 7m), x = 1 on group g0 only: y = 64 B[m][o][g0]."""
+    n_mat, out_dim, in_dim, nb = 2, 4, 384, 2
+    g = in_dim // 64
+    e = (np.arange(g)[None, None, :] + 3 * np.arange(out_dim)[None, :, None]
+         + 7 * np.arange(n_mat)[:, None, None])
+    b = np.vectorize(pow2_bf16)(e - 20).astype(np.uint16)
+    q = np.zeros((n_mat, out_dim, in_dim), np.uint8)
+    s = np.full_like(b, ONE_BF16)
+    for g0 in range(g):
+        x = np.zeros((n_mat, nb, in_dim), np.float32)
+        x[:, :, 64 * g0:64 * g0 + 64] = 1.0
+        y, _ = gemv(q, s, b, x)
+        want = 64.0 * np.exp2(e[:, :, g0] - 20.0)
+        if not np.array_equal(y, np.broadcast_to(want[:, None, :], y.shape)):
+            return False
+    return True
+
+
+def pin_activation_rows(gemv):
+    """Row r of the output depends on activation row r only; matrices are independent."""
+    q, s, b, x = _case(3, 6, 256, 4, 8)
+    y, _ = gemv(q, s, b, x)
+    perm = np.array([2, 0, 3, 1])
+    yp, _ = gemv(q, s, b, np.ascontiguousarray(x[:, perm, :]))
+    if not np.array_equal(yp, y[:, perm, :]):
+        return False
+    for m in range(3):
+        ym, _ = gemv(q[m:m + 1], s[m:m + 1], b[m:m + 1], x[m:m + 1])
+        if not np.array_equal(ym[0], y[m]):
+            return False
+    return True
+
+
+def pin_bound(gemv):
+    """bound >= |y| everywhere and bound equals |W| . |x| from the dense reference."""
+    q, s, b, x = _case(2, 11, 256, 2, 9)
+    y, bound = gemv(q, s, b, x)
+    _, br = dense_reference(q, s, b, x)
+    return bool(np.all(bound >= np.abs(y)) and np.allclose(bound, br, rtol=1e-12, atol=0))
+
+
+PINS = [pin_bruteforce, pin_zero_at_midcode, pin_row_sum, pin_one_hot, pin_scale_position,
+        pin_bias_position, pin_activation_rows, pin_bound]
+
+
+def oracle_gemv(q, s, b, x):
+    import oracle
+    return oracle.gemv(q, s, b, x, nthreads=2)
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(oracle_lib, pin):
+    assert pin(oracle_gemv)
+
+
+def test_exact_rational(oracle_lib):
+    """The double oracle agrees with an exact rational evaluation of the definition."""
+    q, s, b, x = _case(1, 3, 128, 2, 11)
+    y, bound = oracle_lib.gemv(q, s, b, x)
+    sf = bf16_torch(s)
+    bf = bf16_torch(b)
+    for r in range(2):
+        for o in range(3):
+            tot = Fraction(0)
+            for i in range(128):
+                w = Fraction(sf[0, o, i // 64]) * int(q[0, o, i]) + Fraction(bf[0, o, i // 64])
+                tot += w * Fraction(float(x[0, r, i]))
+            assert abs(Fraction(y[0, r, o]) - tot) <= Fraction(1e-14) * Fraction(bound[0, r, o])
+
+
+def test_rows_matches_full(oracle_lib):
+    q, s, b, x = _case(2, 13, 192, 3, 12)
+    y, bound = oracle_lib.gemv(q, s, b, x)
+    mats = np.array([0, 1, 1, 0, 1])
+    rows = np.array([0, 12, 5, 7, 0])
+    ys, bs = oracle_lib.gemv_rows(q, s, b, x, mats, rows)
+    assert np.array_equal(ys, y[mats, :, rows])
+    assert np.array_equal(bs, bound[mats, :, rows])
+
+
+def test_rejects_bad_shapes(oracle_lib):
+    q, s, b, x = _case(1, 2, 64, 1, 0)
+    with pytest.raises(ValueError):
+        oracle_lib.gemv(q[:, :, :32], s, b, x)
+    with pytest.raises(ValueError):
+        oracle_lib.gemv(q, s, b, x[:, :, :32])
+    bad = q.copy()
+    bad[0, 0, 0] = 16
+    with pytest.raises(ValueError):
+        oracle_lib.gemv(bad, s, b, x)
+    with pytest.raises(ValueError):
+        oracle_lib.gemv_rows(q, s, b, x, [0], [2])
+
+
+def test_tiny_workload_rel_to_dense(oracle_lib):
+    c = workloads.make_case("tiny")
+    y, bound = oracle_lib.gemv(c["codes"], c["scales"], c["biases"], c["x"])
+    yr, _ = dense_reference(c["codes"], c["scales"], c["biases"], c["x"])
+    assert np.all(np.abs(y - yr) <= 1e-12 * bound)
+
+
+# --------------------------------------------------------------------------------------
+# activation prep oracle
+
+def test_prep_layout_and_sums(oracle_lib):
+    x = (np.arange(2 * 128, dtype=np.float32).reshape(2, 128) - 50.0) * 0.25  # exact in f16
+    xe, xo, xsum = oracle_lib.prepare_x(x)
+    assert np.array_equal(xe.astype(np.float32), x[:, 0::2])
+    assert np.array_equal(xo.astype(np.float32), x[:, 1::2])
+    # chunk c of row n holds elements 32c..32c+31: closed-form arithmetic series sum
+    for n in range(2):
+        for c in range(4):
+            k = np.arange(32 * c, 32 * c + 32) + 128 * n
+            assert xsum[n, c] == float(((k - 50.0) * 0.25).sum())
+
+
+def test_prep_f16_rounding_matches_torch(oracle_lib):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    x[0, :64] = np.ldexp(rng.random(64), rng.integers(-30, -12, 64)).astype(np.float32)
+    # ties: 1 + 2^-11 -> 1 (even), 1 + 3*2^-11 -> 1 + 2^-9, 2^-25 -> 0, 65520 -> inf
+    x[1, :4] = [1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -25, 65520.0]
+    xe, xo, _ = oracle_lib.prepare_x(x)
+    th = torch.from_numpy(x).half().numpy()
+    assert np.array_equal(xe.view(np.uint16), np.ascontiguousarray(th[:, 0::2]).view(np.uint16))
+    assert np.array_equal(xo.view(np.uint16), np.ascontiguousarray(th[:, 1::2]).view(np.uint16))
+    # x[1,0] -> xe[1,0], x[1,1] -> xo[1,0], x[1,2] -> xe[1,1], x[1,3] -> xo[1,1]
+    assert xe[1, 0].view(np.uint16) == 0x3C00
+    assert xo[1, 0].view(np.uint16) == 0x3C02
+    assert xe[1, 1].view(np.uint16) == 0x0000
+    assert np.isinf(xo[1, 1])
+
+
+def test_prep_constant_sum(oracle_lib):
+    x = np.full((1, 96), 0.1, np.float32)
+    _, _, xsum = oracle_lib.prepare_x(x)
+    assert np.all(xsum == 32.0 * float(np.float16(0.1)))
+
+
+# --------------------------------------------------------------------------------------
+# planted mistakes: each mutant of the oracle source must fail at least one pin
+
+MUTANTS = {
+    "dropped_bias_term": ("acc += s * qx + b * xs;", "acc += s * qx;"),
+    "bias_sign": ("acc += s * qx + b * xs;", "acc += s * qx - b * xs;"),
+    "scale_group_shift": ("const double s = bf16_value(srow[g]);",
+                          "const double s = bf16_value(srow[(g + 1) % groups]);"),
+    "bias_reads_scales": ("const double b = bf16_value(brow[g]);",
+                          "const double b = bf16_value(srow[g]);"),
+    "x_transposed": ("const double xv = (double)xr[g * GROUP + j];",
+                     "const double xv = (double)xr[j * groups + g];"),
+    "code_ignores_matrix": ("const uint8_t *qrow = q + (m * out_dim + o) * in_dim;",
+                            "const uint8_t *qrow = q + o * in_dim;"),
+    "x_ignores_row": ("const float *xr = x + (m * nb + r) * in_dim;",
+                      "const float *xr = x + (m * nb) * in_dim;"),
+    "bf16_decode_shift": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+    "bound_signed_bias": ("bnd += fabs(s) * qax + fabs(b) * ax;", "bnd += fabs(s) * qax + b * ax;"),
+    "code_scale_swapped": ("qx += qv * xv;", "qx += (15.0 - qv) * xv;"),
+}
+
+
+def _load_variant(path):
+    lib = ctypes.CDLL(path)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.q4ref_gemv.argtypes = [p, p, p, p, i64, i64, i64, i64, p, p, ctypes.c_int]
+    lib.q4ref_gemv.restype = ctypes.c_int
+
+    def gemv(q, s, b, x):
+        q = np.ascontiguousarray(q, np.uint8)
+        s = np.ascontiguousarray(s, np.uint16)
+        b = np.ascontiguousarray(b, np.uint16)
+        x = np.ascontiguousarray(x, np.float32)
+        n_mat, out_dim, in_dim = q.shape
+        nb = x.shape[1]
+        y = np.empty((n_mat, nb, out_dim))
+        bound = np.empty_like(y)
+        assert lib.q4ref_gemv(q.ctypes.data, s.ctypes.data, b.ctypes.data, x.ctypes.data,
+                              n_mat, out_dim, in_dim, nb, y.ctypes.data, bound.ctypes.data,
+                              1) == 0
+        return y, bound
+    return gemv
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_mutants_are_caught(tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "q4ref.c")).read()
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+        mpath = tmp_path / f"{name}.c"
+        mpath.write_text(src.replace(old, new))
+        so = tmp_path / f"lib{name}.so"
+        subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-pthread", str(mpath), "-o",
+                        str(so), "-lm"], check=True)
+        gemv = _load_variant(str(so))
+        failed = [p.__name__ for p in PINS if not p(gemv)]
+        assert failed, f"mutant {name} passed every pin"
