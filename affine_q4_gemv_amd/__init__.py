@@ -1,0 +1,180 @@
+"""affine_q4_gemv_amd -- affine-Q4 row-batched GEMV for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libq4mv.so`` (declared in ``include/q4mv.h``).
+The functions here have the same names as the C entry points and only marshal arguments:
+they check dtypes, shapes and devices of torch tensors, allocate outputs with torch when the
+caller passes none, and hand raw device pointers and the current HIP stream to the library.
+Every step of the computation runs in the library's HIP kernels; there is no other path. If
+the library cannot be loaded, importing works but every call raises.
+
+Tensor conventions (all on one GPU, contiguous):
+  codes  uint8   [n_mat, out_dim, in_dim]      one 4-bit code per byte
+  w      int32   [n_mat, out_dim, in_dim // 8] packed codes (bit pattern of u32 words)
+  scales bfloat16 [n_mat, out_dim, in_dim // 64] (bias the same)
+  x      float32 [n_rows, in_dim]              n_rows = n_mat * nb
+  xe, xo float16 [n_rows, in_dim // 2]
+  xsum   float32 [n_rows, in_dim // 32]
+  y      float32 [n_mat, nb, out_dim]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq4mv.so")
+
+Q4MV_OK = 0
+PATH_AUTO, PATH_VALU, PATH_VALU_2ROW, PATH_MFMA = 0, 1, 2, 3
+MAX_NB = 16
+MAX_NB_X_IN = 65536
+
+_lib = None
+
+
+class Q4mvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded ``libq4mv.so`` with argument types set (builds it first if absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.q4mv_pack_codes.argtypes = [p, p, i64, p]
+        L.q4mv_prepare_x.argtypes = [p, i32, i32, p, p, p, p]
+        gemv = [p, p, p, p, p, p, p, i32, i32, i32, i32]
+        L.q4mv.argtypes = gemv + [p]
+        L.q4mv_2row.argtypes = gemv + [p]
+        L.q4mv_path.argtypes = gemv + [i32, p]
+        L.q4mv_auto_path.argtypes = [i32, i32, i32]
+        L.q4mv_status_str.argtypes = [i32]
+        L.q4mv_status_str.restype = ctypes.c_char_p
+        L.q4mv_version.argtypes = []
+        for fn in ("q4mv_pack_codes", "q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_path",
+                   "q4mv_auto_path", "q4mv_version"):
+            getattr(L, fn).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().q4mv_status_str(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, dtype, shape, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _check(fn, status):
+    if status != Q4MV_OK:
+        raise Q4mvError(fn, status)
+
+
+def q4mv_pack_codes(codes, w=None, stream=None):
+    """Pack u8 codes [..., in_dim] eight per u32 word, low nibble first -> int32 [..., in_dim/8]."""
+    torch = _torch()
+    if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous():
+        raise ValueError("codes: contiguous uint8 GPU tensor expected")
+    if codes.shape[-1] % 8:
+        raise ValueError("codes: last dimension must be a multiple of 8")
+    shape = (*codes.shape[:-1], codes.shape[-1] // 8)
+    if w is None:
+        w = torch.empty(shape, dtype=torch.int32, device=codes.device)
+    _need(w, torch.int32, shape, "w")
+    _check("q4mv_pack_codes", lib().q4mv_pack_codes(codes.data_ptr(), w.data_ptr(),
+                                                     codes.numel(), _stream(codes, stream)))
+    return w
+
+
+def q4mv_prepare_x(x, xe=None, xo=None, xsum=None, stream=None):
+    """x f32 [n_rows, in_dim] -> (xe, xo f16 [n_rows, in_dim/2], xsum f32 [n_rows, in_dim/32])."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x: expected [n_rows, in_dim]")
+    n, k = x.shape
+    _need(x, torch.float32, (n, k), "x")
+    dev = x.device
+    xe = torch.empty((n, k // 2), dtype=torch.float16, device=dev) if xe is None else xe
+    xo = torch.empty((n, k // 2), dtype=torch.float16, device=dev) if xo is None else xo
+    xsum = torch.empty((n, k // 32), dtype=torch.float32, device=dev) if xsum is None else xsum
+    _need(xe, torch.float16, (n, k // 2), "xe")
+    _need(xo, torch.float16, (n, k // 2), "xo")
+    _need(xsum, torch.float32, (n, k // 32), "xsum")
+    _check("q4mv_prepare_x", lib().q4mv_prepare_x(x.data_ptr(), n, k, xe.data_ptr(),
+                                                   xo.data_ptr(), xsum.data_ptr(),
+                                                   _stream(x, stream)))
+    return xe, xo, xsum
+
+
+def _gemv(fn_name, w, scales, biases, xe, xo, xsum, nb, y, stream, path=None):
+    torch = _torch()
+    if w.dim() != 3:
+        raise ValueError("w: expected [n_mat, out_dim, in_dim/8]")
+    n_mat, out_dim, w8 = w.shape
+    in_dim = w8 * 8
+    _need(w, torch.int32, (n_mat, out_dim, w8), "w")
+    _need(scales, torch.bfloat16, (n_mat, out_dim, in_dim // 64), "scales")
+    _need(biases, torch.bfloat16, (n_mat, out_dim, in_dim // 64), "biases")
+    _need(xe, torch.float16, (n_mat * nb, in_dim // 2), "xe")
+    _need(xo, torch.float16, (n_mat * nb, in_dim // 2), "xo")
+    _need(xsum, torch.float32, (n_mat * nb, in_dim // 32), "xsum")
+    if y is None:
+        y = torch.empty((n_mat, nb, out_dim), dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, (n_mat, nb, out_dim), "y")
+    args = [w.data_ptr(), scales.data_ptr(), biases.data_ptr(), xe.data_ptr(), xo.data_ptr(),
+            xsum.data_ptr(), y.data_ptr(), n_mat, out_dim, in_dim, nb]
+    if path is not None:
+        args.append(int(path))
+    args.append(_stream(w, stream))
+    _check(fn_name, getattr(lib(), fn_name)(*args))
+    return y
+
+
+def q4mv(w, scales, biases, xe, xo, xsum, nb, y=None, stream=None):
+    """y[m, r, o] for all n_mat matrices and nb activation rows (automatic kernel choice)."""
+    return _gemv("q4mv", w, scales, biases, xe, xo, xsum, nb, y, stream)
+
+
+def q4mv_2row(w, scales, biases, xe, xo, xsum, nb, y=None, stream=None):
+    """Two output rows per lane group; bitwise equal to :func:`q4mv`. out_dim must be even."""
+    return _gemv("q4mv_2row", w, scales, biases, xe, xo, xsum, nb, y, stream)
+
+
+def q4mv_path(w, scales, biases, xe, xo, xsum, nb, path, y=None, stream=None):
+    """:func:`q4mv` with an explicit kernel (PATH_VALU, PATH_VALU_2ROW, PATH_MFMA)."""
+    return _gemv("q4mv_path", w, scales, biases, xe, xo, xsum, nb, y, stream, path=path)
+
+
+def q4mv_auto_path(in_dim: int, nb: int, two_row: bool = False) -> int:
+    return lib().q4mv_auto_path(int(in_dim), int(nb), int(bool(two_row)))
+
+
+def q4mv_version() -> int:
+    return lib().q4mv_version()

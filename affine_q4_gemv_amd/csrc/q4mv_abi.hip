@@ -1,0 +1,166 @@
+// C ABI of libq4mv: argument validation (all on the host, before any launch) and dispatch.
+#include "../../include/q4mv.h"
+#include "q4mv_internal.h"
+
+#include <mutex>
+
+namespace q4mv_impl {
+
+// nb up to this value runs on the VALU dot-product kernels, above it on the MFMA kernel.
+constexpr int kValuAutoMaxNB = 3;
+
+int auto_path(int in_dim, int nb, bool two_row)
+{
+    (void)in_dim;
+    if (nb > kValuAutoMaxNB) return kMfma;
+    return two_row ? kValu2 : kValu1;
+}
+
+int device_cus()
+{
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+hipError_t ensure_lds(const void *fn, size_t bytes)
+{
+    if (bytes <= 64 * 1024) return hipSuccess;
+    static std::mutex mu;
+    static const void *fns[256];
+    static size_t sizes[256];
+    static int n = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; i++)
+        if (fns[i] == fn && sizes[i] >= bytes) return hipSuccess;
+    hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e == hipSuccess && n < 256) {
+        fns[n] = fn;
+        sizes[n] = kMaxLds;
+        n++;
+    }
+    return e;
+}
+
+}  // namespace q4mv_impl
+
+using namespace q4mv_impl;
+
+static inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_gemv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                      const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+                      int out_dim, int in_dim, int nb)
+{
+    if (!w || !scales || !biases || !xe || !xo || !xsum || !y) return Q4MV_ERR_NULL;
+    if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
+        nb > Q4MV_MAX_NB || (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(scales, 2) ||
+        !aligned(biases, 2) || !aligned(xsum, 4) || !aligned(y, 4))
+        return Q4MV_ERR_ALIGN;
+    return Q4MV_OK;
+}
+
+static int run_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                    const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+                    int out_dim, int in_dim, int nb, int path, void *stream)
+{
+    int st = check_gemv(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb);
+    if (st != Q4MV_OK) return st;
+    if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
+    if (path == kAuto) path = auto_path(in_dim, nb, false);
+    if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
+    if (path == kMfma && mfma_lds_bytes(in_dim, nb) > kMaxLds) return Q4MV_ERR_SHAPE;
+    GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
+               static_cast<hipStream_t>(stream)};
+    hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
+extern "C" {
+
+int q4mv_pack_codes(const uint8_t *codes, uint32_t *w, int64_t n_codes, void *stream)
+{
+    if (!codes || !w) return Q4MV_ERR_NULL;
+    if (n_codes < 8 || n_codes % 8 != 0) return Q4MV_ERR_SHAPE;
+    if (!aligned(codes, 8) || !aligned(w, 4)) return Q4MV_ERR_ALIGN;
+    hipError_t e = launch_pack(codes, w, n_codes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
+int q4mv_prepare_x(const float *x, int n_rows, int in_dim, void *xe, void *xo, float *xsum,
+                   void *stream)
+{
+    if (!x || !xe || !xo || !xsum) return Q4MV_ERR_NULL;
+    if (n_rows < 1 || in_dim < 64 || in_dim % 64 != 0) return Q4MV_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(xsum, 4))
+        return Q4MV_ERR_ALIGN;
+    hipError_t e = launch_prep(x, n_rows, in_dim, xe, xo, xsum, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
+int q4mv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, const void *xe,
+         const void *xo, const float *xsum, float *y, int n_mat, int out_dim, int in_dim,
+         int nb, void *stream)
+{
+    return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
+                    auto_path(in_dim, nb, false), stream);
+}
+
+int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+              const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+              int out_dim, int in_dim, int nb, void *stream)
+{
+    int st = check_gemv(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb);
+    if (st != Q4MV_OK) return st;
+    if (out_dim & 1) return Q4MV_ERR_ODD_ROWS;
+    return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
+                    auto_path(in_dim, nb, true), stream);
+}
+
+int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+              const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+              int out_dim, int in_dim, int nb, int path, void *stream)
+{
+    return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb, path,
+                    stream);
+}
+
+int q4mv_auto_path(int in_dim, int nb, int two_row)
+{
+    if (in_dim < 64 || in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB ||
+        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        return Q4MV_ERR_SHAPE;
+    return auto_path(in_dim, nb, two_row != 0);
+}
+
+const char *q4mv_status_str(int status)
+{
+    switch (status) {
+    case Q4MV_OK: return "ok";
+    case Q4MV_ERR_NULL: return "a required pointer is NULL";
+    case Q4MV_ERR_SHAPE: return "a size is out of range";
+    case Q4MV_ERR_ODD_ROWS: return "out_dim must be even for the two-row kernel";
+    case Q4MV_ERR_ALIGN: return "a pointer is not aligned as required";
+    case Q4MV_ERR_LAUNCH: return "the HIP kernel launch failed";
+    case Q4MV_ERR_PATH: return "unknown kernel path";
+    default: return "unknown status";
+    }
+}
+
+int q4mv_version(void) { return 100; }
+
+}  // extern "C"

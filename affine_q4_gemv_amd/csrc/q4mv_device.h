@@ -1,0 +1,76 @@
+// Device-side helpers shared by the GEMV kernels of libq4mv (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4mv_impl {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// 2^24 and 2^-24. A code nibble masked into an f16 lane without an exponent is the f16
+// subnormal q * 2^-24 (exact); the kernels accumulate in those units and rescale once.
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kTwoM24 = 5.9604644775390625e-08f;
+
+// bf16 bit pattern (in the low 16 bits) -> f32: the bits are the high half of the f32.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// a.lo*b.lo + a.hi*b.hi + c with f16 inputs and f32 accumulation (v_dot2c_f32_f16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                  c, false);
+}
+
+// LDS layout of staged activations ("pair layout").
+// For activation row r, chunk c (32 columns) and word J (8 columns 32c+8J .. 32c+8J+7) one
+// 16-byte unit holds four f16 pairs
+//   P0 = (x0, x4), P1 = (x1, x5), P2 = (x2, x6), P3 = (x3, x7)
+// matching how a u32 word of codes is split by masks: (w & 0x000F000F) gives codes 0 and 4,
+// (w & 0x00F000F0) codes 1 and 5 (times 16), and the same on w >> 8 gives 2, 6 and 3, 7.
+// Units are swizzled so that 8 consecutive chunks (same r, J) or 8 consecutive rows (same
+// c, J) land on 8 distinct 16-byte bank quads: no ds_read_b128 bank conflicts in either
+// kernel's access pattern.
+__device__ __forceinline__ int x_unit(int r, int c, int J, int C)
+{
+    return (r * C + (c ^ (r & 1))) * 4 + ((J + (c >> 1) + (r >> 1)) & 3);
+}
+
+// Build the four pairs of one word from the even/odd f16 streams:
+// e = (x0, x2 | x4, x6), o = (x1, x3 | x5, x7) as two u32 each.
+__device__ __forceinline__ uint4 make_pairs(uint2 e, uint2 o)
+{
+    uint4 p;
+    p.x = (e.x & 0xFFFFu) | (e.y << 16);
+    p.y = (o.x & 0xFFFFu) | (o.y << 16);
+    p.z = (e.x >> 16) | (e.y & 0xFFFF0000u);
+    p.w = (o.x >> 16) | (o.y & 0xFFFF0000u);
+    return p;
+}
+
+// DPP helpers (row = 16 lanes). quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over an aligned group of G = 2^log2g lanes. Every lane of the group ends with the same
+// bits (each step adds a value to its partner's value; IEEE addition commutes), and the
+// order of additions depends only on G, so a given row always reduces identically.
+__device__ __forceinline__ float group_sum(float v, int log2g)
+{
+    if (log2g >= 1) v += dpp<0xB1>(v);
+    if (log2g >= 2) v += dpp<0x4E>(v);
+    if (log2g >= 3) v += dpp<0x141>(v);
+    if (log2g >= 4) v += dpp<0x140>(v);
+    if (log2g >= 5) v += __shfl_xor(v, 16, 64);
+    if (log2g >= 6) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+}  // namespace q4mv_impl

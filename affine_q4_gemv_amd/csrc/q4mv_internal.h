@@ -1,0 +1,55 @@
+// Internal (host-side) interface between the C ABI and the kernel launchers of libq4mv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4mv_impl {
+
+struct GemvArgs {
+    const uint32_t *w;
+    const uint16_t *scales;
+    const uint16_t *biases;
+    const void *xe;
+    const void *xo;
+    const float *xsum;
+    float *y;
+    int n_mat, out_dim, in_dim, nb;
+    hipStream_t stream;
+};
+
+// Kernel paths (same numbering as q4mv_path in q4mv.h).
+enum Path { kAuto = 0, kValu1 = 1, kValu2 = 2, kMfma = 3 };
+
+// Lanes per output row for the VALU kernels: the largest power of two <= 64 dividing the
+// number of 32-code chunks per row, so that every lane owns the same number of chunks.
+inline int valu_log2g(int in_dim)
+{
+    const int chunks = in_dim / 32;
+    int l = 0;
+    while (l < 6 && (chunks % (2 << l)) == 0) l++;
+    return l;
+}
+
+int auto_path(int in_dim, int nb, bool two_row);
+
+hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s);
+hipError_t launch_prep(const float *x, int n_rows, int in_dim, void *xe, void *xo, float *xsum,
+                       hipStream_t s);
+hipError_t launch_valu(const GemvArgs &a, int rows);
+hipError_t launch_mfma(const GemvArgs &a);
+
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Largest dynamic LDS a block may use on gfx950.
+constexpr size_t kMaxLds = 160 * 1024;
+// LDS bytes of the MFMA kernel for a shape: staged f16 activations + per-group sums.
+inline size_t mfma_lds_bytes(int in_dim, int nb)
+{
+    return (size_t)nb * (in_dim / 32) * 64 + (size_t)(in_dim / 64) * 16 * 4;
+}
+// Raise a kernel's dynamic LDS limit above the 64 KB default (once per kernel and size).
+hipError_t ensure_lds(const void *fn, size_t bytes);
+
+}  // namespace q4mv_impl

@@ -1,0 +1,137 @@
+/*
+ * q4mv.h -- C ABI of libq4mv.so, the affine-Q4 row-batched matrix-vector engine for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Constant BATCH_MSL page, quantized_rows section, fn_q4_rows_h and the
+ * prefill helper fn_qmv_small_b): for each matrix m, activation row r < nb and output o,
+ *
+ *   y[m][r][o] = sum_g ( S[m][o][g] * sum_{j<64} q[m][o][64g+j] * x[m][r][64g+j]
+ *                      + B[m][o][g] * sum_{j<64} x[m][r][64g+j] )
+ *
+ * i.e. the dequantised weight W = S*q + B (4-bit code q in 0..15, bf16 scale S and bias B per
+ * 64-wide group) times nb activation rows.
+ *
+ * Conventions for every entry point:
+ *  - All pointers are HIP device pointers owned by the caller. The library allocates,
+ *    frees and synchronises nothing, and keeps no state between calls (reentrant).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously on it; errors raised by the device later surface on that stream.
+ *  - Layouts are contiguous and row-major. Sizes are element counts.
+ *  - Every argument is validated on the host before anything is launched. On failure the
+ *    function returns a negative status and enqueues nothing.
+ *  - Inputs are read-only. Outputs are written only inside their stated extent.
+ */
+#ifndef Q4MV_H
+#define Q4MV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    Q4MV_OK = 0,
+    Q4MV_ERR_NULL = -1,     /* a required pointer is NULL */
+    Q4MV_ERR_SHAPE = -2,    /* a size is out of range (see each function) */
+    Q4MV_ERR_ODD_ROWS = -3, /* q4mv_2row with an odd out_dim */
+    Q4MV_ERR_ALIGN = -4,    /* a pointer is not aligned as required */
+    Q4MV_ERR_LAUNCH = -5,   /* the HIP launch reported an error */
+    Q4MV_ERR_PATH = -6      /* q4mv_path: unknown kernel path */
+};
+
+/* Largest activation batch accepted (rows per matrix). */
+#define Q4MV_MAX_NB 16
+/* nb * in_dim must not exceed this: the activations of one matrix are staged in LDS as
+   f16 (2 bytes each), and one staging must fit in the 160 KB of a gfx950 compute unit. */
+#define Q4MV_MAX_NB_X_IN 65536
+
+/*
+ * q4mv_pack_codes -- pack 4-bit codes eight per u32 word, low nibble first.
+ *
+ * Layout (Constant BATCH_MSL page, fn_qmv_small_b, which reads code i of a word at bits
+ * 4i..4i+3; the same order as the 4-bit pack of TQ_QUANT on the inferencelayer forward.rs
+ * page): word k holds codes 8k..8k+7, code 8k+i in bits [4i, 4i+4).
+ *   codes : u8  [n_codes]   one code per byte; only bits 0..3 of each byte are used.
+ *   w     : u32 [n_codes/8] output.
+ * A matrix of codes u8 [n_mat][out_dim][in_dim] packs into the w layout that q4mv reads.
+ * Errors: NULL pointer; n_codes < 8 or n_codes % 8 != 0 (SHAPE); codes not 8-byte or w not
+ * 4-byte aligned (ALIGN).
+ */
+int q4mv_pack_codes(const uint8_t *codes, uint32_t *w, int64_t n_codes, void *stream);
+
+/*
+ * q4mv_prepare_x -- activation prep for the GEMV.
+ *
+ * Constant BATCH_MSL page, fn_norm_prep_b (its prep half) and fn_moe_act_b: x is split into
+ * f16 even/odd streams, and each 32-element chunk gets one sum, taken over the same
+ * f16-rounded values the dot products use.
+ *   x    : f32 [n_rows][in_dim]
+ *   xe   : f16 [n_rows][in_dim/2]   xe[n][k] = f16(x[n][2k])     (round to nearest even)
+ *   xo   : f16 [n_rows][in_dim/2]   xo[n][k] = f16(x[n][2k+1])
+ *   xsum : f32 [n_rows][in_dim/32]  xsum[n][c] = sum_{i<32} f16(x[n][32c+i]) (f32 sum)
+ * For q4mv, n_rows = n_mat * nb and matrix m uses rows m*nb .. m*nb+nb-1.
+ * Errors: NULL pointer; n_rows < 1, in_dim < 64 or in_dim % 64 != 0 (SHAPE); x, xe or xo
+ * not 16-byte aligned, xsum not 4-byte aligned (ALIGN).
+ */
+int q4mv_prepare_x(const float *x, int n_rows, int in_dim, void *xe, void *xo, float *xsum,
+                   void *stream);
+
+/*
+ * q4mv -- the affine-Q4 GEMV over n_mat independent matrices and nb activation rows each.
+ *
+ *   w       : u32 [n_mat][out_dim][in_dim/8]   packed codes (q4mv_pack_codes layout)
+ *   scales  : u16 [n_mat][out_dim][in_dim/64]  bf16 bit patterns
+ *   biases  : u16 [n_mat][out_dim][in_dim/64]  bf16 bit patterns
+ *   xe, xo, xsum : from q4mv_prepare_x with n_rows = n_mat*nb
+ *   y       : f32 [n_mat][nb][out_dim]          fully overwritten, nothing written beyond
+ * Matrix m reads activation rows m*nb .. m*nb+nb-1 (the expert layout of fn_moe_down_b on
+ * the Constant BATCH_MSL page: expert u's rows start at u*NB).
+ * Accumulation is f32 throughout. For a given (in_dim, nb) the result does not depend on
+ * out_dim, n_mat, or which entry point (q4mv / q4mv_2row) is used: bitwise identical.
+ * Errors: NULL pointer; n_mat < 1, out_dim < 1, in_dim < 64, in_dim % 64 != 0,
+ * nb outside 1..Q4MV_MAX_NB, nb*in_dim > Q4MV_MAX_NB_X_IN (SHAPE); w, xe or xo not 16-byte
+ * aligned, scales/biases not 2-byte, xsum/y not 4-byte aligned (ALIGN); launch failure.
+ */
+int q4mv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, const void *xe,
+         const void *xo, const float *xsum, float *y, int n_mat, int out_dim, int in_dim,
+         int nb, void *stream);
+
+/*
+ * q4mv_2row -- same contract and bitwise-identical result; each lane group of a wavefront
+ * owns two consecutive output rows and shares every activation read between them (the
+ * two-row helper fn_q4_2rows_h and fn_moe_down_b on the Constant BATCH_MSL page). Pays off
+ * on short rows (the 640-wide expert down projection).
+ * Extra error: out_dim odd (ODD_ROWS).
+ */
+int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+              const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+              int out_dim, int in_dim, int nb, void *stream);
+
+/*
+ * q4mv_path -- q4mv with an explicit kernel choice instead of the nb-based dispatch.
+ *   path 0: automatic (what q4mv does), 1: VALU dot-product kernel, one row per lane group,
+ *   2: VALU kernel, two rows per lane group (q4mv_2row; out_dim must be even),
+ *   3: MFMA kernel (16x16x32 f16 matrix cores; activation rows padded to 16).
+ * Same arguments, layouts and errors as q4mv, plus PATH for an unknown path. For testing
+ * and measurement of every kernel at every nb.
+ */
+int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+              const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+              int out_dim, int in_dim, int nb, int path, void *stream);
+
+/* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
+   (two_row = 1) takes for this shape; a negative status if the shape is invalid. */
+int q4mv_auto_path(int in_dim, int nb, int two_row);
+
+/* Static English text for a status code. */
+const char *q4mv_status_str(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int q4mv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4MV_H */

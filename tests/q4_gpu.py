@@ -1,0 +1,60 @@
+"""Helpers for the GPU tests: move generated inputs to the device through the library's own
+entry points, run a kernel path, and judge parity against the oracle."""
+import numpy as np
+import torch
+
+import affine_q4_gemv_amd as q4
+
+REL_L2 = 1e-3       # relative L2 error over all outputs
+ELEM = 2e-3         # per element: |err| <= ELEM * sum_i(|S q x| + |B x|)
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def bf16_tensor(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.to(dev()).view(torch.bfloat16)
+
+
+def upload(case):
+    """codes -> packed words on the device (q4mv_pack_codes), scales/biases, x -> prep."""
+    codes = torch.from_numpy(case["codes"]).to(dev())
+    w = q4.q4mv_pack_codes(codes)
+    del codes
+    s = bf16_tensor(case["scales"])
+    b = bf16_tensor(case["biases"])
+    n_mat, nb, in_dim = case["x"].shape
+    x = torch.from_numpy(case["x"].reshape(n_mat * nb, in_dim)).to(dev())
+    xe, xo, xsum = q4.q4mv_prepare_x(x)
+    return dict(w=w, s=s, b=b, x=x, xe=xe, xo=xo, xsum=xsum, nb=nb)
+
+
+def run(d, path=q4.PATH_AUTO, y=None):
+    if path == "2row":
+        out = q4.q4mv_2row(d["w"], d["s"], d["b"], d["xe"], d["xo"], d["xsum"], d["nb"], y=y)
+    elif path == q4.PATH_AUTO:
+        out = q4.q4mv(d["w"], d["s"], d["b"], d["xe"], d["xo"], d["xsum"], d["nb"], y=y)
+    else:
+        out = q4.q4mv_path(d["w"], d["s"], d["b"], d["xe"], d["xo"], d["xsum"], d["nb"], path,
+                           y=y)
+    torch.cuda.synchronize()
+    return out
+
+
+def parity(y_gpu, y_ref, bound, what=""):
+    """Both halves of the tolerance; returns (rel_l2, worst per-element ratio)."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref)
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
+    nref = np.linalg.norm(y_ref)
+    rel = np.linalg.norm(err) / nref if nref > 0 else np.linalg.norm(err)
+    ratio = np.max(err / (ELEM * bound + 1e-300)) if err.size else 0.0
+    assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
+    assert ratio <= 1.0, f"{what}: per-element error {ratio:.3f}x the bound"
+    return rel, ratio
+
+
+def flush(msg):
+    print(msg, flush=True)

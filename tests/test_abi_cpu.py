@@ -1,0 +1,112 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and
+rejects invalid arguments on the host with the documented status, launching nothing."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4mv.h")
+
+OK, ENULL, ESHAPE, EODD, EALIGN, ELAUNCH, EPATH = 0, -1, -2, -3, -4, -5, -6
+A = 0x10000  # a 16-byte aligned fake address: validation fails before anything reads it
+
+
+@pytest.fixture(scope="module")
+def L():
+    import affine_q4_gemv_amd as q
+    return q.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q4mv\w*)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    fns = declared_functions()
+    for name in ("q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_pack_codes", "q4mv_path",
+                 "q4mv_auto_path", "q4mv_status_str", "q4mv_version"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    import affine_q4_gemv_amd as q
+    for st in (OK, ENULL, ESHAPE, EODD, EALIGN, ELAUNCH, EPATH):
+        assert q.status_str(st) and q.status_str(st) != "unknown status"
+    assert q.status_str(12345) == "unknown status"
+    assert L.q4mv_version() >= 100
+
+
+def gemv_args(**kw):
+    a = dict(w=A, s=A, b=A, xe=A, xo=A, xsum=A, y=A, n_mat=1, out=8, ind=128, nb=1)
+    a.update(kw)
+    return [a["w"], a["s"], a["b"], a["xe"], a["xo"], a["xsum"], a["y"], a["n_mat"], a["out"],
+            a["ind"], a["nb"]]
+
+
+@pytest.mark.parametrize("fn", ["q4mv", "q4mv_2row"])
+def test_gemv_validation(L, fn):
+    f = getattr(L, fn)
+    for k in ("w", "s", "b", "xe", "xo", "xsum", "y"):
+        assert f(*gemv_args(**{k: None}), None) == ENULL
+    for kw in (dict(n_mat=0), dict(out=0), dict(ind=0), dict(ind=96), dict(ind=32),
+               dict(nb=0), dict(nb=17), dict(nb=16, ind=4160), dict(ind=-64)):
+        assert f(*gemv_args(**kw), None) == ESHAPE, kw
+    for kw in (dict(w=A + 4), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1), dict(b=A + 1),
+               dict(xsum=A + 2), dict(y=A + 1)):
+        assert f(*gemv_args(**kw), None) == EALIGN, kw
+
+
+def test_two_row_needs_even_rows(L):
+    assert L.q4mv_2row(*gemv_args(out=7), None) == EODD
+    assert L.q4mv_path(*gemv_args(out=7), 2, None) == EODD
+
+
+def test_path_validation(L):
+    assert L.q4mv_path(*gemv_args(), 4, None) == EPATH
+    assert L.q4mv_path(*gemv_args(), -1, None) == EPATH
+    assert L.q4mv_path(*gemv_args(nb=0), 1, None) == ESHAPE
+
+
+def test_prep_validation(L):
+    f = L.q4mv_prepare_x
+    assert f(None, 1, 128, A, A, A, None) == ENULL
+    assert f(A, 1, 128, A, None, A, None) == ENULL
+    assert f(A, 0, 128, A, A, A, None) == ESHAPE
+    assert f(A, 1, 96, A, A, A, None) == ESHAPE
+    assert f(A + 4, 1, 128, A, A, A, None) == EALIGN
+    assert f(A, 1, 128, A + 8, A, A, None) == EALIGN
+    assert f(A, 1, 128, A, A, A + 2, None) == EALIGN
+
+
+def test_pack_validation(L):
+    f = L.q4mv_pack_codes
+    assert f(None, A, 64, None) == ENULL
+    assert f(A, A, 12, None) == ESHAPE
+    assert f(A, A, 0, None) == ESHAPE
+    assert f(A + 4, A, 64, None) == EALIGN
+    assert f(A, A + 2, 64, None) == EALIGN
+
+
+def test_auto_path(L):
+    assert L.q4mv_auto_path(2560, 1, 0) == 1
+    assert L.q4mv_auto_path(640, 1, 1) == 2
+    assert L.q4mv_auto_path(2560, 16, 0) == 3
+    assert L.q4mv_auto_path(2560, 16, 1) == 3
+    assert L.q4mv_auto_path(96, 1, 0) == ESHAPE
+    assert L.q4mv_auto_path(8192, 16, 0) == ESHAPE
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import affine_q4_gemv_amd as q
+    with pytest.raises(ValueError):
+        q.q4mv_prepare_x(torch.zeros(1, 128))
