@@ -54,6 +54,29 @@ hipError_t ensure_lds(const void *fn, size_t bytes)
     return e;
 }
 
+int resident_blocks(const void *fn, int threads, size_t lds)
+{
+    static std::mutex mu;
+    struct Ent {
+        const void *fn;
+        int threads;
+        size_t lds;
+        int blocks;
+    };
+    static Ent ents[512];
+    static int n = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; i++)
+        if (ents[i].fn == fn && ents[i].threads == threads && ents[i].lds == lds)
+            return ents[i].blocks;
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, threads, lds) != hipSuccess ||
+        blocks < 1)
+        blocks = 1;
+    if (n < 512) ents[n++] = Ent{fn, threads, lds, blocks};
+    return blocks;
+}
+
 }  // namespace q4mv_impl
 
 using namespace q4mv_impl;

@@ -61,15 +61,32 @@ __device__ __forceinline__ float dpp(float v)
 
 // Sum over an aligned group of G = 2^log2g lanes. Every lane of the group ends with the same
 // bits (each step adds a value to its partner's value; IEEE addition commutes), and the
-// order of additions depends only on G, so a given row always reduces identically.
+// order of additions depends only on G, so a given row always reduces identically. The
+// steps past log2g add +0.0 instead of branching: straight-line code keeps the compiler from
+// splitting (and reordering work around) the caller's loop body.
+template <int LOG2G>
+__device__ __forceinline__ float group_sum_ct(float v)
+{
+    if constexpr (LOG2G >= 1) v += dpp<0xB1>(v);
+    if constexpr (LOG2G >= 2) v += dpp<0x4E>(v);
+    if constexpr (LOG2G >= 3) v += dpp<0x141>(v);
+    if constexpr (LOG2G >= 4) v += dpp<0x140>(v);
+    if constexpr (LOG2G >= 5) v += __shfl_xor(v, 16, 64);
+    if constexpr (LOG2G >= 6) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Runtime-G form of group_sum_ct (same additions in the same order).
 __device__ __forceinline__ float group_sum(float v, int log2g)
 {
-    if (log2g >= 1) v += dpp<0xB1>(v);
-    if (log2g >= 2) v += dpp<0x4E>(v);
-    if (log2g >= 3) v += dpp<0x141>(v);
-    if (log2g >= 4) v += dpp<0x140>(v);
-    if (log2g >= 5) v += __shfl_xor(v, 16, 64);
-    if (log2g >= 6) v += __shfl_xor(v, 32, 64);
+    v += log2g >= 1 ? dpp<0xB1>(v) : 0.0f;
+    v += log2g >= 2 ? dpp<0x4E>(v) : 0.0f;
+    v += log2g >= 3 ? dpp<0x141>(v) : 0.0f;
+    v += log2g >= 4 ? dpp<0x140>(v) : 0.0f;
+    const float a = __shfl_xor(v, 16, 64);
+    v += log2g >= 5 ? a : 0.0f;
+    const float b = __shfl_xor(v, 32, 64);
+    v += log2g >= 6 ? b : 0.0f;
     return v;
 }
 

@@ -51,5 +51,7 @@ inline size_t mfma_lds_bytes(int in_dim, int nb)
 }
 // Raise a kernel's dynamic LDS limit above the 64 KB default (once per kernel and size).
 hipError_t ensure_lds(const void *fn, size_t bytes);
+// Blocks of `fn` that can be resident on one CU at this block size and LDS (cached).
+int resident_blocks(const void *fn, int threads, size_t lds);
 
 }  // namespace q4mv_impl

@@ -28,14 +28,26 @@ namespace q4mv_impl {
 
 constexpr int kValuThreads = 256;
 constexpr int kValuMaxNB = 8;  // nb > 8 runs as two launches over activation-row ranges
+// Launch shape (compile-time tunables, measured on MI355X): persistent blocks per CU, and
+// whether a wave loads its next row step while computing the current one.
+#ifndef Q4MV_VALU_BLOCKS_PER_CU
+#define Q4MV_VALU_BLOCKS_PER_CU 4
+#endif
+#ifndef Q4MV_VALU_PREFETCH
+#define Q4MV_VALU_PREFETCH 0
+#endif
+constexpr bool kValuPrefetch = Q4MV_VALU_PREFETCH != 0;
 
-template <int NB, int ROWS, int CPL>
+// LOG2G, CPL > 0: lane-group size and chunks per lane fixed at compile time (the common row
+// lengths); LOG2G = -1, CPL = 0: both taken at run time (any in_dim).
+template <int NB, int ROWS, int LOG2G, int CPL>
 __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
-    int out_dim, int in_dim, int nb_total, int r0, int log2g, int cpl_rt)
+    int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt)
 {
+    const int log2g = LOG2G >= 0 ? LOG2G : log2g_rt;
     extern __shared__ uint4 lds[];
     constexpr bool XREG = CPL > 0 && NB * CPL <= 4;
     const int m = blockIdx.y;
@@ -43,23 +55,39 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     const int groups = in_dim >> 6;
     const int words8 = in_dim >> 3;  // uint2 units (4 halves) per activation row
 
-    // ---- stage activation rows r0 .. r0+NB-1 of matrix m (pair layout + scaled sums)
-    {
+    // Stage activation rows r0 .. r0+NB-1 of matrix m (pair layout + scaled sums). Called
+    // after each wave has issued its first weight loads, so the two latencies overlap.
+    auto stage = [&]() {
         const size_t xrow0 = (size_t)m * nb_total + r0;
         const uint2 *xe_m = xe + xrow0 * words8;
         const uint2 *xo_m = xo + xrow0 * words8;
-        const int units = NB * C * 4;
-        for (int u = threadIdx.x; u < units; u += kValuThreads) {
-            const int r = u / (C * 4);
-            const int cj = u - r * (C * 4);
-            lds[x_unit(r, cj >> 2, cj & 3, C)] =
-                make_pairs(xe_m[(size_t)r * words8 + cj], xo_m[(size_t)r * words8 + cj]);
-        }
-        float *xs = reinterpret_cast<float *>(lds + NB * C * 4);
         const float *xsum_m = xsum + xrow0 * C;
-        for (int u = threadIdx.x; u < NB * C; u += kValuThreads) xs[u] = xsum_m[u] * kTwoM24;
-    }
-    __syncthreads();
+        float *xsw = reinterpret_cast<float *>(lds + NB * C * 4);
+        const int units = NB * C * 4;  // 16-byte pair units; NB*C chunk sums
+        // each round issues all of its loads before any LDS write: one memory round trip
+        for (int base = threadIdx.x; base < units; base += 4 * kValuThreads) {
+            uint2 e[4], o[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int u = min(base + i * kValuThreads, units - 1);
+                const int r = u / (C * 4), cj = u - r * (C * 4);
+                e[i] = xe_m[(size_t)r * words8 + cj];
+                o[i] = xo_m[(size_t)r * words8 + cj];
+            }
+            const int us = (base - threadIdx.x) / 4 + threadIdx.x;  // chunk-sum index
+            const float sv = xsum_m[min(us, NB * C - 1)];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int u = base + i * kValuThreads;
+                if (u < units) {
+                    const int r = u / (C * 4), cj = u - r * (C * 4);
+                    lds[x_unit(r, cj >> 2, cj & 3, C)] = make_pairs(e[i], o[i]);
+                }
+            }
+            if (us < NB * C) xsw[us] = sv * kTwoM24;
+        }
+        __syncthreads();
+    };
     const float *xs = reinterpret_cast<const float *>(lds + NB * C * 4);
 
     const int lane = threadIdx.x & 63;
@@ -79,28 +107,26 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     // activations in registers for the whole kernel when they fit
     uint4 xr[XREG ? CPL : 1][XREG ? NB : 1][4];
     float xsr[XREG ? CPL : 1][XREG ? NB : 1];
-    if constexpr (XREG) {
+    auto load_xreg = [&]() {
+        if constexpr (XREG) {
 #pragma unroll
-        for (int k = 0; k < CPL; k++) {
-            const int c = j + (k << log2g);
+            for (int k = 0; k < CPL; k++) {
+                const int c = j + (k << log2g);
 #pragma unroll
-            for (int r = 0; r < NB; r++) {
+                for (int r = 0; r < NB; r++) {
 #pragma unroll
-                for (int J = 0; J < 4; J++) xr[k][r][J] = lds[x_unit(r, c, J, C)];
-                xsr[k][r] = xs[r * C + c];
+                    for (int J = 0; J < 4; J++) xr[k][r][J] = lds[x_unit(r, c, J, C)];
+                    xsr[k][r] = xs[r * C + c];
+                }
             }
         }
-    }
+    };
 
-    if constexpr (CPL > 0) {
-        // ---- fully unrolled chunk loop: all loads of a step are issued before any use
-        for (int ws = blockIdx.x * (kValuThreads / 64) + (threadIdx.x >> 6); ws < wave_steps;
-             ws += wstride) {
-            // Compiler fence: keeps the per-step LDS activation reads inside the loop (hoisting
-            // them all out of it multiplies register use and spills).
-            asm volatile("" ::: "memory");
-            uint4 cc[ROWS][CPL];
-            uint32_t sc[ROWS][CPL], bc[ROWS][CPL];
+    if constexpr (CPL > 0 && LOG2G >= 0) {
+        // ---- fully unrolled chunk loop
+        uint4 cc[ROWS][CPL];
+        uint32_t sbc[ROWS][CPL];
+        auto load = [&](int ws, uint4 (&cw)[ROWS][CPL], uint32_t (&sv)[ROWS][CPL]) {
 #pragma unroll
             for (int t = 0; t < ROWS; t++) {
                 const int row = min(ws * rows_per_wave + grp * ROWS + t, out_dim - 1);
@@ -110,12 +136,26 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
 #pragma unroll
                 for (int k = 0; k < CPL; k++) {
                     const int c = j + (k << log2g);
-                    cc[t][k] = wr[c];
-                    sc[t][k] = sr[c >> 1];
-                    bc[t][k] = br[c >> 1];
+                    cw[t][k] = wr[c];
+                    // lanes 2i and 2i+1 own the two chunks of one group: the even lane loads
+                    // the scale, the odd lane the bias, and compute() swaps them with DPP
+                    sv[t][k] = (j & 1) ? br[c >> 1] : sr[c >> 1];
                 }
             }
-
+        };
+        auto compute = [&](int ws) {
+            // scale and bias of each (row, chunk): own value plus the partner lane's
+            float sc[ROWS][CPL], bc[ROWS][CPL];
+#pragma unroll
+            for (int t = 0; t < ROWS; t++)
+#pragma unroll
+                for (int k = 0; k < CPL; k++) {
+                    const uint32_t mine = sbc[t][k];
+                    const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(
+                        0, (int)mine, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+                    sc[t][k] = bf16_to_f32((j & 1) ? other : mine);
+                    bc[t][k] = bf16_to_f32((j & 1) ? mine : other);
+                }
             float acc[ROWS][NB];
 #pragma unroll
             for (int t = 0; t < ROWS; t++)
@@ -125,7 +165,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
             for (int k = 0; k < CPL; k++) {
                 const int c = j + (k << log2g);
                 // per-chunk fence for larger batches: bounds the LDS reads in flight
-                if constexpr (NB > 1) asm volatile("" ::: "memory");
+                if constexpr (NB > 1 || ROWS > 1) asm volatile("" ::: "memory");
                 uint32_t h[ROWS][4][4];
 #pragma unroll
                 for (int t = 0; t < ROWS; t++) {
@@ -163,24 +203,63 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                             ao = dot2(h[t][J][3], xp[J].w, ao);
                         }
                         const float qd = __builtin_fmaf(ao, 0.0625f, ae);
-                        acc[t][r] = __builtin_fmaf(bf16_to_f32(sc[t][k]), qd,
-                                                   __builtin_fmaf(bf16_to_f32(bc[t][k]), xsv,
-                                                                  acc[t][r]));
+                        acc[t][r] = __builtin_fmaf(sc[t][k], qd,
+                                                   __builtin_fmaf(bc[t][k], xsv, acc[t][r]));
                     }
                 }
             }
+            // all reductions first, then the stores (one divergent block at the very end)
 #pragma unroll
-            for (int t = 0; t < ROWS; t++) {
-                const int row = ws * rows_per_wave + grp * ROWS + t;
+            for (int t = 0; t < ROWS; t++)
 #pragma unroll
-                for (int r = 0; r < NB; r++) {
-                    const float v = group_sum(acc[t][r], log2g);
-                    if (j == 0 && row < out_dim) y_m[(size_t)r * out_dim + row] = v * kTwo24;
+                for (int r = 0; r < NB; r++) acc[t][r] = group_sum_ct<LOG2G>(acc[t][r]);
+            if (j == 0) {
+#pragma unroll
+                for (int t = 0; t < ROWS; t++) {
+                    const int row = ws * rows_per_wave + grp * ROWS + t;
+                    if (row < out_dim) {
+#pragma unroll
+                        for (int r = 0; r < NB; r++)
+                            y_m[(size_t)r * out_dim + row] = acc[t][r] * kTwo24;
+                    }
                 }
+            }
+        };
+        int ws = blockIdx.x * (kValuThreads / 64) + (threadIdx.x >> 6);
+        if constexpr (kValuPrefetch) {
+            // next step's codes are in flight while this step computes
+            uint4 cn[ROWS][CPL];
+            uint32_t sn[ROWS][CPL];
+            if (ws < wave_steps) load(ws, cn, sn);
+            stage();
+            load_xreg();
+            for (; ws < wave_steps; ws += wstride) {
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int t = 0; t < ROWS; t++)
+#pragma unroll
+                    for (int k = 0; k < CPL; k++) {
+                        cc[t][k] = cn[t][k];
+                        sbc[t][k] = sn[t][k];
+                    }
+                if (ws + wstride < wave_steps) load(ws + wstride, cn, sn);
+                compute(ws);
+            }
+        } else {
+            if (ws < wave_steps) load(ws, cc, sbc);  // first step's weights, before staging
+            stage();
+            load_xreg();
+            for (bool first = true; ws < wave_steps; ws += wstride, first = false) {
+                // Compiler fence: keeps the per-step LDS activation reads inside the loop
+                // (hoisting them all out of it multiplies register use and spills).
+                asm volatile("" ::: "memory");
+                if (!first) load(ws, cc, sbc);
+                compute(ws);
             }
         }
     } else {
         // ---- generic chunk count: runtime loop in batches of 4 chunks
+        stage();
         for (int ws = blockIdx.x * (kValuThreads / 64) + (threadIdx.x >> 6); ws < wave_steps;
              ws += wstride) {
             asm volatile("" ::: "memory");
@@ -200,12 +279,11 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                 for (int t = 0; t < ROWS; t++)
 #pragma unroll
                     for (int kk = 0; kk < 4; kk++) {
-                        if (k0 + kk < cpl) {
-                            const int c = j + ((k0 + kk) << log2g);
-                            cc[t][kk] = w_m[(size_t)rowc[t] * C + c];
-                            sc[t][kk] = s_m[(size_t)rowc[t] * groups + (c >> 1)];
-                            bc[t][kk] = b_m[(size_t)rowc[t] * groups + (c >> 1)];
-                        }
+                        // clamped, unconditional loads (chunks past cpl are never used)
+                        const int c = j + (min(k0 + kk, cpl - 1) << log2g);
+                        cc[t][kk] = w_m[(size_t)rowc[t] * C + c];
+                        sc[t][kk] = s_m[(size_t)rowc[t] * groups + (c >> 1)];
+                        bc[t][kk] = b_m[(size_t)rowc[t] * groups + (c >> 1)];
                     }
 #pragma unroll
                 for (int kk = 0; kk < 4; kk++) {
@@ -257,33 +335,36 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
 typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, int, int, int);
 
+// (log2 G, CPL) of the specialised row lengths: in_dim = 32 * CPL << log2G.
+#define Q4MV_VALU_SHAPES(X)                                                                   \
+    X(4, 1) /* 512 */ X(2, 5) /* 640 */ X(5, 1) /* 1024 */ X(4, 3) /* 1536 */                 \
+    X(6, 1) /* 2048 */ X(4, 5) /* 2560 */ X(5, 3) /* 3072 */ X(4, 7) /* 3584 */               \
+    X(6, 2) /* 4096 */ X(5, 5) /* 5120 */ X(6, 3) /* 6144 */ X(5, 7) /* 7168 */               \
+    X(6, 4) /* 8192 */ X(6, 7) /* 14336 */
+
 template <int NB, int ROWS>
-static ValuFn pick_cpl(int cpl)
+static ValuFn pick_shape(int log2g, int cpl)
 {
-    switch (cpl) {
-    case 1: return valu_kernel<NB, ROWS, 1>;
-    case 2: return valu_kernel<NB, ROWS, 2>;
-    case 3: return valu_kernel<NB, ROWS, 3>;
-    case 4: return valu_kernel<NB, ROWS, 4>;
-    case 5: return valu_kernel<NB, ROWS, 5>;
-    case 6: return valu_kernel<NB, ROWS, 6>;
-    case 7: return valu_kernel<NB, ROWS, 7>;
-    default: return valu_kernel<NB, ROWS, 0>;
-    }
+#define Q4MV_PICK(L, K) \
+    if (log2g == L && cpl == K) return valu_kernel<NB, ROWS, L, K>;
+    Q4MV_VALU_SHAPES(Q4MV_PICK)
+#undef Q4MV_PICK
+    return valu_kernel<NB, ROWS, -1, 0>;
 }
 
 template <int ROWS>
-static ValuFn pick_nb(int nb, int cpl)
+static ValuFn pick_nb(int nb, int log2g, int cpl)
 {
     switch (nb) {
-    case 1: return pick_cpl<1, ROWS>(cpl);
-    case 2: return pick_cpl<2, ROWS>(cpl);
-    case 3: return pick_cpl<3, ROWS>(cpl);
-    case 4: return pick_cpl<4, ROWS>(cpl);
-    case 5: return pick_cpl<5, ROWS>(cpl);
-    case 6: return pick_cpl<6, ROWS>(cpl);
-    case 7: return pick_cpl<7, ROWS>(cpl);
-    default: return pick_cpl<8, ROWS>(cpl);
+    case 1: return pick_shape<1, ROWS>(log2g, cpl);
+    case 2: return pick_shape<2, ROWS>(log2g, cpl);
+    case 3: return pick_shape<3, ROWS>(log2g, cpl);
+    case 4: return pick_shape<4, ROWS>(log2g, cpl);
+    // larger batches: generic kernel (the MFMA kernel is the fast path there)
+    case 5: return valu_kernel<5, ROWS, -1, 0>;
+    case 6: return valu_kernel<6, ROWS, -1, 0>;
+    case 7: return valu_kernel<7, ROWS, -1, 0>;
+    default: return valu_kernel<8, ROWS, -1, 0>;
     }
 }
 
@@ -292,7 +373,7 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const int log2g = valu_log2g(a.in_dim);
     const int C = a.in_dim / 32;
     const int cpl = C >> log2g;
-    ValuFn fn = rows == 2 ? pick_nb<2>(nbp, cpl) : pick_nb<1>(nbp, cpl);
+    ValuFn fn = rows == 2 ? pick_nb<2>(nbp, log2g, cpl) : pick_nb<1>(nbp, log2g, cpl);
     const size_t lds = (size_t)nbp * C * 64 + (size_t)nbp * C * 4;
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
@@ -300,7 +381,10 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const long wave_steps = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
     const long blocks_needed = (wave_steps + 3) / 4;
     // persistent blocks: enough to fill every CU a few times over, shared by the matrices
-    const long cap = std::max(1L, (long)device_cus() * 4 / a.n_mat);
+    const long per_cu = std::min<long>(Q4MV_VALU_BLOCKS_PER_CU,
+                                       resident_blocks(reinterpret_cast<const void *>(fn),
+                                                       kValuThreads, lds));
+    const long cap = std::max(1L, (long)device_cus() * per_cu / a.n_mat);
     const long gx = std::max(1L, std::min(blocks_needed, cap));
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(kValuThreads), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
