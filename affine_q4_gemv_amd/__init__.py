@@ -53,7 +53,7 @@ def lib():
         L.q4mv.argtypes = gemv + [p]
         L.q4mv_2row.argtypes = gemv + [p]
         L.q4mv_path.argtypes = gemv + [i32, p]
-        L.q4mv_auto_path.argtypes = [i32, i32, i32]
+        L.q4mv_auto_path.argtypes = [i32, i32, i32, i32]
         L.q4mv_status_str.argtypes = [i32]
         L.q4mv_status_str.restype = ctypes.c_char_p
         L.q4mv_version.argtypes = []
@@ -172,8 +172,8 @@ def q4mv_path(w, scales, biases, xe, xo, xsum, nb, path, y=None, stream=None):
     return _gemv("q4mv_path", w, scales, biases, xe, xo, xsum, nb, y, stream, path=path)
 
 
-def q4mv_auto_path(in_dim: int, nb: int, two_row: bool = False) -> int:
-    return lib().q4mv_auto_path(int(in_dim), int(nb), int(bool(two_row)))
+def q4mv_auto_path(in_dim: int, nb: int, two_row: bool = False, out_dim: int = 2) -> int:
+    return lib().q4mv_auto_path(int(in_dim), int(nb), int(bool(two_row)), int(out_dim))
 
 
 def q4mv_version() -> int:

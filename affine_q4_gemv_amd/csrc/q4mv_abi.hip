@@ -6,14 +6,18 @@
 
 namespace q4mv_impl {
 
-// nb up to this value runs on the VALU dot-product kernels, above it on the MFMA kernel.
+// nb up to this value runs on the VALU dot-product kernels, above it on the MFMA kernel
+// (measured crossover on MI355X).
 constexpr int kValuAutoMaxNB = 3;
 
-int auto_path(int in_dim, int nb, bool two_row)
+// The automatic choice for q4mv: MFMA for larger batches; otherwise the two-row VALU kernel
+// when out_dim is even (it is bitwise identical to the one-row kernel and faster), else the
+// one-row kernel.
+int auto_path(int in_dim, int nb, bool two_row, int out_dim)
 {
     (void)in_dim;
     if (nb > kValuAutoMaxNB) return kMfma;
-    return two_row ? kValu2 : kValu1;
+    return two_row || out_dim % 2 == 0 ? kValu2 : kValu1;
 }
 
 int device_cus()
@@ -104,9 +108,9 @@ static int run_path(const uint32_t *w, const uint16_t *scales, const uint16_t *b
     int st = check_gemv(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb);
     if (st != Q4MV_OK) return st;
     if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
-    if (path == kAuto) path = auto_path(in_dim, nb, false);
+    if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
     if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
-    if (path == kMfma && mfma_lds_bytes(in_dim, nb) > kMaxLds) return Q4MV_ERR_SHAPE;
+    if (path == kMfma && mfma_tiles_per_block(in_dim, nb) == 0) return Q4MV_ERR_SHAPE;
     GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
                static_cast<hipStream_t>(stream)};
     hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
@@ -140,7 +144,7 @@ int q4mv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, cons
          int nb, void *stream)
 {
     return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
-                    auto_path(in_dim, nb, false), stream);
+                    auto_path(in_dim, nb, false, out_dim), stream);
 }
 
 int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
@@ -151,7 +155,7 @@ int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
     if (st != Q4MV_OK) return st;
     if (out_dim & 1) return Q4MV_ERR_ODD_ROWS;
     return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
-                    auto_path(in_dim, nb, true), stream);
+                    auto_path(in_dim, nb, true, out_dim), stream);
 }
 
 int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
@@ -162,12 +166,13 @@ int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
                     stream);
 }
 
-int q4mv_auto_path(int in_dim, int nb, int two_row)
+int q4mv_auto_path(int in_dim, int nb, int two_row, int out_dim)
 {
     if (in_dim < 64 || in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB ||
-        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN || out_dim < 1)
         return Q4MV_ERR_SHAPE;
-    return auto_path(in_dim, nb, two_row != 0);
+    if (two_row && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
+    return auto_path(in_dim, nb, two_row != 0, out_dim);
 }
 
 const char *q4mv_status_str(int status)

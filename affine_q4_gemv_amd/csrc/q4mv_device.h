@@ -9,6 +9,7 @@ namespace q4mv_impl {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
 
 // 2^24 and 2^-24. A code nibble masked into an f16 lane without an exponent is the f16
 // subnormal q * 2^-24 (exact); the kernels accumulate in those units and rescale once.

@@ -31,7 +31,7 @@ inline int valu_log2g(int in_dim)
     return l;
 }
 
-int auto_path(int in_dim, int nb, bool two_row);
+int auto_path(int in_dim, int nb, bool two_row, int out_dim);
 
 hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s);
 hipError_t launch_prep(const float *x, int n_rows, int in_dim, void *xe, void *xo, float *xsum,
@@ -44,11 +44,21 @@ int device_cus();
 
 // Largest dynamic LDS a block may use on gfx950.
 constexpr size_t kMaxLds = 160 * 1024;
-// LDS bytes of the MFMA kernel for a shape: staged f16 activations + per-group sums.
+// LDS bytes of the MFMA kernel for a shape: staged f16 activations + per-group sums (the
+// partial-sum buffers of mfma_part_bytes come on top).
 inline size_t mfma_lds_bytes(int in_dim, int nb)
 {
-    return (size_t)nb * (in_dim / 32) * 64 + (size_t)(in_dim / 64) * 16 * 4;
+    // nb rows of 4C + 1 pair units, then groups x 16 sums
+    return (size_t)nb * (4 * (in_dim / 32) + 1) * 16 + (size_t)(in_dim / 64) * 16 * 4;
 }
+// Partial-sum buffers of the MFMA kernel: 2 steps x tiles per block x 3 quarters x 64 lanes.
+inline size_t mfma_part_bytes(int tpb, bool nb16)
+{
+    return (size_t)2 * tpb * 3 * 64 * (nb16 ? 8 : 4) * 4;
+}
+// Tiles (of 32 output rows) per block of the MFMA kernel for a shape; 0 if the shape's LDS
+// does not fit in one compute unit.
+int mfma_tiles_per_block(int in_dim, int nb);
 // Raise a kernel's dynamic LDS limit above the 64 KB default (once per kernel and size).
 hipError_t ensure_lds(const void *fn, size_t bytes);
 // Blocks of `fn` that can be resident on one CU at this block size and LDS (cached).

@@ -125,8 +125,9 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     if constexpr (CPL > 0 && LOG2G >= 0) {
         // ---- fully unrolled chunk loop
         uint4 cc[ROWS][CPL];
-        uint32_t sbc[ROWS][CPL];
-        auto load = [&](int ws, uint4 (&cw)[ROWS][CPL], uint32_t (&sv)[ROWS][CPL]) {
+        uint32_t scb[ROWS][CPL], bcb[ROWS][CPL];
+        auto load = [&](int ws, uint4 (&cw)[ROWS][CPL], uint32_t (&sv)[ROWS][CPL],
+                        uint32_t (&bv)[ROWS][CPL]) {
 #pragma unroll
             for (int t = 0; t < ROWS; t++) {
                 const int row = min(ws * rows_per_wave + grp * ROWS + t, out_dim - 1);
@@ -137,24 +138,19 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                 for (int k = 0; k < CPL; k++) {
                     const int c = j + (k << log2g);
                     cw[t][k] = wr[c];
-                    // lanes 2i and 2i+1 own the two chunks of one group: the even lane loads
-                    // the scale, the odd lane the bias, and compute() swaps them with DPP
-                    sv[t][k] = (j & 1) ? br[c >> 1] : sr[c >> 1];
+                    sv[t][k] = sr[c >> 1];
+                    bv[t][k] = br[c >> 1];
                 }
             }
         };
         auto compute = [&](int ws) {
-            // scale and bias of each (row, chunk): own value plus the partner lane's
             float sc[ROWS][CPL], bc[ROWS][CPL];
 #pragma unroll
             for (int t = 0; t < ROWS; t++)
 #pragma unroll
                 for (int k = 0; k < CPL; k++) {
-                    const uint32_t mine = sbc[t][k];
-                    const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(
-                        0, (int)mine, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-                    sc[t][k] = bf16_to_f32((j & 1) ? other : mine);
-                    bc[t][k] = bf16_to_f32((j & 1) ? mine : other);
+                    sc[t][k] = bf16_to_f32(scb[t][k]);
+                    bc[t][k] = bf16_to_f32(bcb[t][k]);
                 }
             float acc[ROWS][NB];
 #pragma unroll
@@ -229,8 +225,8 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
         if constexpr (kValuPrefetch) {
             // next step's codes are in flight while this step computes
             uint4 cn[ROWS][CPL];
-            uint32_t sn[ROWS][CPL];
-            if (ws < wave_steps) load(ws, cn, sn);
+            uint32_t sn[ROWS][CPL], bn[ROWS][CPL];
+            if (ws < wave_steps) load(ws, cn, sn, bn);
             stage();
             load_xreg();
             for (; ws < wave_steps; ws += wstride) {
@@ -240,20 +236,21 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
 #pragma unroll
                     for (int k = 0; k < CPL; k++) {
                         cc[t][k] = cn[t][k];
-                        sbc[t][k] = sn[t][k];
+                        scb[t][k] = sn[t][k];
+                        bcb[t][k] = bn[t][k];
                     }
-                if (ws + wstride < wave_steps) load(ws + wstride, cn, sn);
+                if (ws + wstride < wave_steps) load(ws + wstride, cn, sn, bn);
                 compute(ws);
             }
         } else {
-            if (ws < wave_steps) load(ws, cc, sbc);  // first step's weights, before staging
+            if (ws < wave_steps) load(ws, cc, scb, bcb);  // first step's weights, before staging
             stage();
             load_xreg();
             for (bool first = true; ws < wave_steps; ws += wstride, first = false) {
                 // Compiler fence: keeps the per-step LDS activation reads inside the loop
                 // (hoisting them all out of it multiplies register use and spills).
                 asm volatile("" ::: "memory");
-                if (!first) load(ws, cc, sbc);
+                if (!first) load(ws, cc, scb, bcb);
                 compute(ws);
             }
         }

@@ -2,21 +2,32 @@
 
 One step = q4mv_prepare_x (activation prep) + q4mv (the GEMV) over one batch of synthetic
 inputs already resident in HBM. Weights rotate over R copies whose total exceeds twice the
-256 MB Infinity Cache, so every launch streams its weights from HBM.
+256 MB Infinity Cache, so every launch streams its weights from HBM. Timed loops are captured
+in a HIP graph (replayed after a warm-up replay), so host launch cost is not measured; a
+replay's output is checked bit for bit against an eager call.
 
-Prints ONE JSON line (rank 0). `value` is weight GB/s of the whole step (weight bytes of the
-matrix / step time). `roofline` is the GEMV kernel alone: algorithmic bytes (weights +
-activations read + outputs written) per launch / its average duration, timed with HIP events
-around each launch inside the timed region. `cpu_baseline` is the CPU oracle timed on the host
-cores on the same workload. `sweep` repeats the kernel timing at the other activation batch
-sizes of the metric (NB = 1/4/8, and 16 for the LM head) and on the MLP up projection.
+Prints ONE JSON line. `value` is weight GB/s of the whole step (weight bytes / step time).
+`roofline` is the GEMV kernel alone: algorithmic bytes (weights + activations read + outputs
+written) per launch / its average duration, timed with HIP events around a graph of
+back-to-back GEMV launches on the launch stream. `cpu_baseline` is the CPU oracle on the host
+cores on the same workload. `sweep` repeats the kernel timing at the other batch sizes of the
+metric (NB = 1/4/8, 16 for the LM head) and on the other projection shapes.
+
+Profiling helpers (commands recorded in profiles/):
+  --eager               time plain launches (for rocprofv3 runs)
+  --pmc-probe           a plain 256 MiB streaming kernel (negation), then 10 GEMV launches:
+                        the counters of the first calibrate those of the second
+  --summarize-trace D   kernel statistics of a rocprofv3 --kernel-trace run directory
+  --summarize-pmc F W   HBM traffic per GEMV launch from FETCH_SIZE / WRITE_SIZE run dirs
 """
 import argparse
-import hashlib
+import csv
 import glob
+import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -25,30 +36,34 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 600e6  # > 2 x (256 MB Infinity Cache + L2)
+CALIB_BYTES = 256 << 20
 METRIC = "affine-Q4 GEMV weight GB/s and % of HBM peak at NB=1/4/8; rows/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4mv_traffic.json")
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {"valu_kernel": ["q4mv_valu.hip"], "mfma_kernel": ["q4mv_mfma.hip"]}
+
+
+def kernel_source_hash(kernel):
+    """Hash of the sources that define a kernel and its launch shape."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "affine_q4_gemv_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for f in KERNEL_SOURCES[kernel] + ["q4mv_device.h", "q4mv_internal.h"]:
+        h.update(open(os.path.join(ROOT, "affine_q4_gemv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, nb):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "q4mv_traffic.json")
-    if not os.path.exists(path):
+def load_traffic(workload, nb, kernel):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current sources of that kernel (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
-        d = json.load(open(path))
+        ent = json.load(open(TRAFFIC_FILE)).get(f"{workload}_nb{nb}")
     except ValueError:
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if not ent or ent.get("kernel") != kernel or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
-    ent = d.get("runs", {}).get(f"{workload}_nb{nb}")
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    return ent.get("hbm_bytes_per_launch")
 
 
 class Problem:
@@ -62,8 +77,8 @@ class Problem:
         import workloads
 
         self.q4, self.torch = q4, torch
-        self.case = workloads.make_case(name, nb=nb)
-        c = self.case
+        c = workloads.make_case(name, nb=nb)
+        self.name = name
         self.n_mat, self.out_dim, self.in_dim, self.nb = c["n_mat"], c["out_dim"], c["in_dim"], nb
         self.weight_bytes = workloads.weight_bytes(self.n_mat, self.out_dim, self.in_dim)
         dev = torch.device("cuda:0")
@@ -82,12 +97,22 @@ class Problem:
         self.x = torch.from_numpy(c["x"].reshape(self.n_mat * nb, self.in_dim)).to(dev)
         self.xe, self.xo, self.xsum = q4.q4mv_prepare_x(self.x)
         self.y = torch.empty((self.n_mat, nb, self.out_dim), dtype=torch.float32, device=dev)
-        # algorithmic bytes of one GEMV launch: weights + staged activations read + outputs
         rows = self.n_mat * nb
-        self.act_bytes = rows * (self.in_dim * 2 + self.in_dim // 32 * 4)
-        self.out_bytes = rows * self.out_dim * 4
-        self.algo_bytes = self.weight_bytes + self.act_bytes + self.out_bytes
+        self.algo_bytes = self.algorithmic_bytes(name, nb)
+        self.path = q4.q4mv_auto_path(self.in_dim, nb, False, self.out_dim)
+        self.kernel = "mfma_kernel" if self.path == q4.PATH_MFMA else "valu_kernel"
+        del c
         torch.cuda.synchronize()
+
+    @staticmethod
+    def algorithmic_bytes(name, nb):
+        """Weights + staged activations read + outputs written by one GEMV launch."""
+        import workloads
+        w = workloads.WORKLOADS[name]
+        n_mat, out_dim, in_dim = w["n_mat"], w["out_dim"], w["in_dim"]
+        rows = n_mat * nb
+        return (workloads.weight_bytes(n_mat, out_dim, in_dim)
+                + rows * (in_dim * 2 + in_dim // 32 * 4) + rows * out_dim * 4)
 
     def prep(self):
         self.q4.q4mv_prepare_x(self.x, self.xe, self.xo, self.xsum)
@@ -97,41 +122,78 @@ class Problem:
         self.q4.q4mv(self.w[k], self.s[k], self.b[k], self.xe, self.xo, self.xsum, self.nb,
                      y=self.y)
 
+    def _graph(self, body, n):
+        """Capture n iterations of body(i) in a HIP graph (after one eager warm-up)."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(2):
+                body(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                body(i)
+        return g
+
+    def _time_graph(self, g, n, warmup_replays=1, reps=3):
+        torch = self.torch
+        for _ in range(warmup_replays):
+            g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / n)
+        return statistics.median(ts)
+
+    def check_graph_output(self):
+        """The graph's result equals an eager call bit for bit (weights copies are equal)."""
+        torch = self.torch
+        got = self.y.clone()
+        self.prep()
+        self.gemv(0)
+        torch.cuda.synchronize()
+        if not torch.equal(got, self.y):
+            raise RuntimeError("graph replay output differs from the eager call")
+
     def time_steps(self, steps, warmup):
-        """(ms per full step, avg GEMV kernel ms) with HIP events on the launch stream."""
+        """ms per full step (prep + GEMV), graph-captured."""
+        def step(i):
+            self.prep()
+            self.gemv(i)
+        g = self._graph(step, steps)
+        ms = self._time_graph(g, steps, warmup_replays=max(1, math.ceil(warmup / steps)))
+        self.check_graph_output()
+        return ms
+
+    def time_kernel(self, launches=200):
+        """Average GEMV kernel ms over a graph of back-to-back launches."""
+        g = self._graph(self.gemv, launches)
+        ms = self._time_graph(g, launches)
+        self.check_graph_output()
+        return ms
+
+    def time_eager(self, steps, warmup):
         torch = self.torch
         for i in range(warmup):
             self.prep()
             self.gemv(i)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t0.record()
+        a.record()
         for i in range(steps):
             self.prep()
-            ev[i][0].record()
             self.gemv(i)
-            ev[i][1].record()
-        t1.record()
+        b.record()
         torch.cuda.synchronize()
-        step_ms = t0.elapsed_time(t1) / steps
-        kern_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-        return step_ms, kern_ms
-
-    def time_kernel(self, launches, warmup=20):
-        """Average GEMV kernel ms over back-to-back launches (activations already prepped)."""
-        torch = self.torch
-        for i in range(warmup):
-            self.gemv(i)
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record()
-        for i in range(launches):
-            self.gemv(i)
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / launches
+        return a.elapsed_time(b) / steps
 
 
 def cpu_baseline(name, nb, reps=3):
@@ -147,13 +209,109 @@ def cpu_baseline(name, nb, reps=3):
         times.append(time.perf_counter() - t)
         if times[-1] > 10.0:
             break
-    t = sorted(times)[len(times) // 2]
+    t = statistics.median(times)
     return {"value": round(wbytes / t / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"full workload ({c['n_mat']}x{c['out_dim']}x{c['in_dim']}, NB={nb}), "
                       f"double-precision C oracle with {threads} threads, median of "
-                      f"{len(times)} runs of {t:.3f} s"}
+                      f"{len(times)} runs ({t:.3f} s each)"}
 
+
+# --------------------------------------------------------------------------------------
+# profile summaries
+
+def _read_csv_rows(run_dir, suffix):
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "**", f"*{suffix}"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_trace(run_dir, out, cmd):
+    rows = _read_csv_rows(run_dir, "kernel_stats.csv")
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {run_dir}")
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}",
+             "# columns: calls, total_ns, average_ns, min_ns, max_ns, percent, kernel"]
+    for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+        lines.append(f"{r.get('Calls')}, {r.get('TotalDurationNs')}, {r.get('AverageNs')}, "
+                     f"{r.get('MinNs')}, {r.get('MaxNs')}, {r.get('Percentage')}, {r.get('Name')}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _pmc_by_kernel(run_dir, counter):
+    rows = _read_csv_rows(run_dir, "counter_collection.csv")
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, nb, cmd, out_txt):
+    """FETCH_SIZE / WRITE_SIZE are in KiB per dispatch. Each is scaled by the factor that
+    makes it read exactly the known bytes of the plain streaming kernel in the same
+    process (256 MiB read and 256 MiB written)."""
+    fetch = _pmc_by_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_by_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        return (ks[0], statistics.median(d[ks[0]]) * 1024.0) if ks else (None, None)
+    _, cf = pick(fetch, "neg_kernel")
+    _, cw = pick(write, "neg_kernel")
+    kernel = "valu_kernel" if any("valu_kernel" in k for k in fetch) else "mfma_kernel"
+    kname, kf = pick(fetch, kernel)
+    _, kw = pick(write, kernel)
+    if None in (cf, cw, kf, kw):
+        raise SystemExit(f"missing counters: copy {cf} {cw} kernel {kf} {kw}")
+    sf, sw = CALIB_BYTES / cf, CALIB_BYTES / cw
+    entry = {"kernel": kernel, "source_hash": kernel_source_hash(kernel),
+             "fetch_bytes_counter": kf, "write_bytes_counter": kw, "fetch_scale": sf,
+             "write_scale": sw, "hbm_bytes_per_launch": round(kf * sf + kw * sw),
+             "command": cmd}
+    d = {}
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            d = json.load(open(TRAFFIC_FILE))
+        except ValueError:
+            d = {}
+    d[f"{workload}_nb{nb}"] = entry
+    json.dump(d, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    p = Problem.algorithmic_bytes(workload, nb)
+    lines = [f"# HBM traffic of {kname.split('(')[0]} on {workload} NB={nb}",
+             f"# command (twice, COUNTER = FETCH_SIZE, then WRITE_SIZE): {cmd}",
+             f"calibration kernel (torch neg, {CALIB_BYTES} B read + {CALIB_BYTES} B written): "
+             f"FETCH_SIZE {cf / 1024:.1f} KiB -> scale {sf:.4f}; "
+             f"WRITE_SIZE {cw / 1024:.1f} KiB -> scale {sw:.4f}",
+             f"GEMV kernel, median over {len(fetch[kname])} launches: "
+             f"FETCH_SIZE {kf / 1024:.1f} KiB, WRITE_SIZE {kw / 1024:.1f} KiB",
+             f"scaled HBM bytes per launch: read {kf * sf:.0f}, written {kw * sw:.0f}, "
+             f"total {kf * sf + kw * sw:.0f}",
+             f"algorithmic bytes per launch: {p} (ratio {(kf * sf + kw * sw) / p:.4f})"]
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def pmc_probe(workload, nb):
+    import torch
+    src = torch.full((CALIB_BYTES // 4,), 1.0, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)  # one kernel that reads and writes exactly CALIB_BYTES
+    torch.cuda.synchronize()
+    del src, dst
+    p = Problem(workload, nb)
+    for i in range(10):
+        p.gemv(i)
+    torch.cuda.synchronize()
+    print("pmc probe done", flush=True)
+
+
+# --------------------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -164,7 +322,17 @@ def main():
     ap.add_argument("--nb", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sweep", action="store_true", help="skip the NB / shape sweep")
+    ap.add_argument("--eager", action="store_true", help="time plain launches (profiling)")
+    ap.add_argument("--pmc-probe", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--out")
+    ap.add_argument("--cmd", default="")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.out, args.cmd)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, args.workload, args.nb, args.cmd, args.out)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the GEMV shards by output rows "
               "with no cross-GPU step in the kernel); run it with --gpus 1", file=sys.stderr)
@@ -174,16 +342,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.pmc_probe:
+        return pmc_probe(args.workload, args.nb)
 
     prob = Problem(args.workload, args.nb)
-    step_ms, kern_ms = prob.time_steps(args.steps, args.warmup)
+    if args.eager:
+        step_ms = prob.time_eager(args.steps, args.warmup)
+        kern_ms = step_ms
+    else:
+        step_ms = prob.time_steps(args.steps, args.warmup)
+        kern_ms = prob.time_kernel(args.steps)
     value = prob.weight_bytes / (step_ms * 1e-3) / 1e9
     achieved = prob.algo_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, args.nb)
-    import affine_q4_gemv_amd as q4
-    path = q4.q4mv_auto_path(prob.in_dim, prob.nb, False)
-    kernel_name = {1: "valu_kernel", 2: "valu_kernel", 3: "mfma_kernel"}.get(path, "?")
-
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -201,32 +371,33 @@ def main():
                                f"affine-Q4 group 64, NB={prob.nb}",
                    "n_mat": prob.n_mat, "out_dim": prob.out_dim, "in_dim": prob.in_dim,
                    "nb": prob.nb, "group": 64, "weight_bytes": prob.weight_bytes,
-                   "rotation_copies": prob.R, "seed": 0,
+                   "rotation_copies": prob.R, "seed": 0, "graph_captured": not args.eager,
                    "operands": "u4 codes, bf16 scale+bias per 64, f16 activations, f32 acc"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "rows_per_s": round(prob.n_mat * prob.out_dim / (step_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": kernel_name,
+                     "traffic": load_traffic(args.workload, args.nb, prob.kernel),
+                     "kernel": prob.kernel,
                      "kernel_us": round(kern_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": prob.algo_bytes},
     }
     del prob
     torch.cuda.empty_cache()
 
-    if not args.no_sweep:
+    if not args.no_sweep and not args.eager:
         sweep = []
         runs = [("lm_head", nb) for nb in (1, 4, 8, 16)] + [("up", nb) for nb in (1, 4, 8)] + \
-               [("moe_down", 4), ("dense", 1)]
+               [("moe_down", 4), ("dense", 1), ("dense", 4), ("dense", 8)]
         for name, nb in runs:
             p = Problem(name, nb)
             ms = p.time_kernel(200)
+            gbps = p.weight_bytes / (ms * 1e-3) / 1e9
             sweep.append({"workload": name, "nb": nb, "kernel_us": round(ms * 1e3, 3),
-                          "weight_GBps": round(p.weight_bytes / (ms * 1e-3) / 1e9, 1),
-                          "pct_hbm_peak": round(100 * p.weight_bytes / (ms * 1e-3) / 1e9 /
-                                                HBM_PEAK_GBPS, 1),
+                          "weight_GBps": round(gbps, 1),
+                          "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
                           "rows_per_s": round(p.n_mat * p.out_dim / (ms * 1e-3), 1),
-                          "path": q4.q4mv_auto_path(p.in_dim, nb, False)})
+                          "path": p.path})
             del p
             torch.cuda.empty_cache()
         result["sweep"] = sweep

@@ -112,17 +112,21 @@ int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
  * q4mv_path -- q4mv with an explicit kernel choice instead of the nb-based dispatch.
  *   path 0: automatic (what q4mv does), 1: VALU dot-product kernel, one row per lane group,
  *   2: VALU kernel, two rows per lane group (q4mv_2row; out_dim must be even),
- *   3: MFMA kernel (16x16x32 f16 matrix cores; activation rows padded to 16).
- * Same arguments, layouts and errors as q4mv, plus PATH for an unknown path. For testing
- * and measurement of every kernel at every nb.
+ *   3: MFMA kernel (32x32x16 f16 matrix cores; activation rows padded to 32).
+ * Same arguments, layouts and errors as q4mv, plus PATH for an unknown path, and SHAPE when
+ * path 3 is asked for a shape whose activations and sums do not fit in LDS
+ * (about 2*nb*in_dim + in_dim bytes; only nb <= 2 with very long rows). For testing and
+ * measurement of every kernel at every nb.
  */
 int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
               int out_dim, int in_dim, int nb, int path, void *stream);
 
 /* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
-   (two_row = 1) takes for this shape; a negative status if the shape is invalid. */
-int q4mv_auto_path(int in_dim, int nb, int two_row);
+   (two_row = 1) takes for this shape; a negative status if the shape is invalid. For small
+   nb, q4mv runs the two-row kernel whenever out_dim is even (the results are bitwise the
+   same as the one-row kernel's), and nb > 3 runs on the MFMA kernel. */
+int q4mv_auto_path(int in_dim, int nb, int two_row, int out_dim);
 
 /* Static English text for a status code. */
 const char *q4mv_status_str(int status);

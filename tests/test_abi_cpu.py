@@ -97,12 +97,16 @@ def test_pack_validation(L):
 
 
 def test_auto_path(L):
-    assert L.q4mv_auto_path(2560, 1, 0) == 1
-    assert L.q4mv_auto_path(640, 1, 1) == 2
-    assert L.q4mv_auto_path(2560, 16, 0) == 3
-    assert L.q4mv_auto_path(2560, 16, 1) == 3
-    assert L.q4mv_auto_path(96, 1, 0) == ESHAPE
-    assert L.q4mv_auto_path(8192, 16, 0) == ESHAPE
+    assert L.q4mv_auto_path(2560, 1, 0, 9) == 1    # odd out_dim: one-row kernel
+    assert L.q4mv_auto_path(2560, 1, 0, 10) == 2   # even out_dim: two-row kernel
+    assert L.q4mv_auto_path(640, 1, 1, 2560) == 2
+    assert L.q4mv_auto_path(2560, 3, 0, 2560) == 2
+    assert L.q4mv_auto_path(2560, 4, 0, 2560) == 3
+    assert L.q4mv_auto_path(2560, 16, 1, 2560) == 3
+    assert L.q4mv_auto_path(640, 1, 1, 7) == EODD
+    assert L.q4mv_auto_path(96, 1, 0, 8) == ESHAPE
+    assert L.q4mv_auto_path(8192, 16, 0, 8) == ESHAPE
+    assert L.q4mv_auto_path(2560, 1, 0, 0) == ESHAPE
 
 
 def test_binding_rejects_cpu_tensors():
