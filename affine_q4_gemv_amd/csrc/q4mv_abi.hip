@@ -10,14 +10,17 @@ namespace q4mv_impl {
 // (measured crossover on MI355X).
 constexpr int kValuAutoMaxNB = 3;
 
-// The automatic choice for q4mv: MFMA for larger batches; otherwise the two-row VALU kernel
-// when out_dim is even (it is bitwise identical to the one-row kernel and faster), else the
-// one-row kernel.
+// The automatic choice: MFMA for larger batches. Below that, q4mv_2row runs the two-row
+// kernel; q4mv runs one activation row on the one-row kernel (on MI355X it is as fast or
+// faster at every measured shape, the 640-wide expert down projection included) and 2..3
+// rows on the two-row kernel when out_dim is even. The one-row and two-row kernels give
+// bitwise the same result, so q4mv and q4mv_2row agree whichever they take.
 int auto_path(int in_dim, int nb, bool two_row, int out_dim)
 {
     (void)in_dim;
     if (nb > kValuAutoMaxNB) return kMfma;
-    return two_row || out_dim % 2 == 0 ? kValu2 : kValu1;
+    if (two_row) return kValu2;
+    return nb > 1 && out_dim % 2 == 0 ? kValu2 : kValu1;
 }
 
 int device_cus()
@@ -110,7 +113,8 @@ static int run_path(const uint32_t *w, const uint16_t *scales, const uint16_t *b
     if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
     if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
     if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
-    if (path == kMfma && mfma_tiles_per_block(in_dim, nb) == 0) return Q4MV_ERR_SHAPE;
+    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_mat * ((out_dim + 31) / 32)).wpb == 0)
+        return Q4MV_ERR_SHAPE;
     GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
                static_cast<hipStream_t>(stream)};
     hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);

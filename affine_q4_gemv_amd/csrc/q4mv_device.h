@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef Q4MV_DOT2_FIRST_ASM
+#define Q4MV_DOT2_FIRST_ASM 1
+#endif
+
 namespace q4mv_impl {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -24,6 +28,19 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
                                   c, false);
+}
+
+// a.lo*b.lo + a.hi*b.hi with a zero accumulator, as one VOP3P instruction (the builtin with
+// c = 0 becomes a move of zero plus v_dot2c). Same operation and rounding as dot2(a, b, 0).
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b)
+{
+#if Q4MV_DOT2_FIRST_ASM
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+#else
+    return dot2(a, b, 0.0f);
+#endif
 }
 
 // LDS layout of staged activations ("pair layout").

@@ -51,14 +51,16 @@ inline size_t mfma_lds_bytes(int in_dim, int nb)
     // nb rows of 4C + 1 pair units, then groups x 16 sums
     return (size_t)nb * (4 * (in_dim / 32) + 1) * 16 + (size_t)(in_dim / 64) * 16 * 4;
 }
-// Partial-sum buffers of the MFMA kernel: 2 steps x tiles per block x 3 quarters x 64 lanes.
-inline size_t mfma_part_bytes(int tpb, bool nb16)
+// Partial-sum buffers of the MFMA kernel: 2 steps x tile groups per block x (ks - 1) parts
+// x 64 lanes x accumulators.
+inline size_t mfma_part_bytes(int wpb, int ks, bool nb16)
 {
-    return (size_t)2 * tpb * 3 * 64 * (nb16 ? 8 : 4) * 4;
+    return (size_t)2 * (wpb / ks) * (ks - 1) * 64 * (nb16 ? 8 : 4) * 4;
 }
-// Tiles (of 32 output rows) per block of the MFMA kernel for a shape; 0 if the shape's LDS
-// does not fit in one compute unit.
-int mfma_tiles_per_block(int in_dim, int nb);
+// Launch shape of the MFMA kernel: waves per block and waves per tile (K-split); {0, 0} if
+// the shape's LDS does not fit in one compute unit.
+struct MfmaShape { int wpb, ks; };
+MfmaShape mfma_shape(int in_dim, int nb, long tiles);
 // Raise a kernel's dynamic LDS limit above the 64 KB default (once per kernel and size).
 hipError_t ensure_lds(const void *fn, size_t bytes);
 // Blocks of `fn` that can be resident on one CU at this block size and LDS (cached).

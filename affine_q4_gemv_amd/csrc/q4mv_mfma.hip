@@ -12,25 +12,26 @@
 // quantized_rows section). The dequantised weight is never formed (the page's tiled expert
 // GEMM dequantises to f16 tiles instead), and no cross-lane shuffle of codes is needed.
 //
-// Work split: the 4 waves of a tile group share one 32-row tile, each taking a quarter of
-// the row's scale groups; their partial sums meet in LDS and are added in a fixed order
-// (quarter 0 + 1 + 2 + 3), so results do not depend on the grid. A block holds TPB tile
-// groups and strides over tiles; the finer work unit keeps CUs evenly loaded. Loads are
-// unconditional (indices clamped) and double-buffered in batches of KB groups across tile
-// boundaries, so a wave always has its next batch in flight while it computes.
+// Work split: KS waves (a tile group) share one 32-row tile, each taking a contiguous part
+// of the row's scale groups; with KS > 1 their partial sums meet in LDS and are added in a
+// fixed order (part 0 + 1 + ...), so results do not depend on the grid. KS is 1 when there
+// are enough tiles to fill the GPU (no partial sums, no barrier after staging) and 2 or 4
+// for short output dimensions. A block holds WPB / KS tile groups and strides over tiles.
+// Loads are unconditional (indices clamped) and issued in batches of KB groups.
 #include "q4mv_device.h"
 #include "q4mv_internal.h"
 
 #include <algorithm>
 
 // Launch shape and pipelining (compile-time tunables, measured on MI355X): the cap on blocks
-// per CU; tiles per block for small and large LDS footprints; double-buffered weight loads
+// per CU; the tile counts below which the K-split is 2 and 4 (measured: 4 is best down to
+// NB = 1 even for the LM head's 4748 tiles); double-buffered weight loads
 // across units; A operands read one group ahead.
-#ifndef Q4MV_MFMA_TPB_SMALL
-#define Q4MV_MFMA_TPB_SMALL 1
+#ifndef Q4MV_MFMA_KS2_BELOW
+#define Q4MV_MFMA_KS2_BELOW (1 << 30)
 #endif
-#ifndef Q4MV_MFMA_TPB_BIG
-#define Q4MV_MFMA_TPB_BIG 4
+#ifndef Q4MV_MFMA_KS4_BELOW
+#define Q4MV_MFMA_KS4_BELOW (1 << 30)
 #endif
 #ifndef Q4MV_MFMA_PINGPONG
 #define Q4MV_MFMA_PINGPONG 0
@@ -44,18 +45,24 @@
 
 namespace q4mv_impl {
 
-// TPB: tiles per block (4 waves each). KB: groups per load batch (even). NB16: activation
+// Waves per block: 8 (two per SIMD); with the per-lane register budget of 8-wave blocks the
+// kernels stay in VGPRs (no AGPR spill area), so the CU can hold several blocks when LDS
+// allows.
+constexpr int kMfmaWaves = 8;
+
+// WPB: waves per block. KS: waves per tile (K-split). KB: groups per load batch (even). NB16: activation
 // rows 8..15 are live (nb > 8). SMODE: 1 = even group count and 4-byte aligned scale and
 // bias arrays, a group pair is one dword; 0 = 2-byte loads.
 // CLAMP: the row has fewer groups than KB, so group indices are clamped to the row.
-template <int TPB, int KB, bool NB16, int SMODE, bool CLAMP>
-__global__ __launch_bounds__(TPB * 256) void mfma_kernel(
+template <int WPB, int KS, int KB, bool NB16, int SMODE, bool CLAMP>
+__global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
     int out_dim, int in_dim, int nb)
 {
-    constexpr int TH = TPB * 256;
+    constexpr int TH = WPB * 64;
+    constexpr int TPB = WPB / KS;  // tile groups per block
     constexpr int NACC = NB16 ? 8 : 4;
     extern __shared__ uint4 lds[];
     const int m = blockIdx.y;
@@ -64,7 +71,7 @@ __global__ __launch_bounds__(TPB * 256) void mfma_kernel(
     const int words8 = in_dim >> 3;
 
     // LDS: activations | group sums xsg[g][16] * 2^-24 | partial sums
-    // part[2][TPB][3][64][NACC] (double-buffered by tile step).
+    // part[2][TPB][KS-1][64][NACC] (double-buffered by tile step).
     // Activation layout: row r, chunk c has four 16-byte units at r*RS + 4c + u,
     //   u = 0: (x0,x4)(x2,x6) of word 0, then of word 1   -- even code positions
     //   u = 1: (x1,x5)(x3,x7) of word 0, then of word 1   -- odd code positions
@@ -127,17 +134,17 @@ __global__ __launch_bounds__(TPB * 256) void mfma_kernel(
     const int h = lane >> 5;  // which chunk of the group this lane holds
     // wave index, made visibly wave-uniform so everything derived from it lives in SGPRs
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slot = wv >> 2;    // tile group of this wave within the block
-    const int quarter = wv & 3;  // which quarter of the groups this wave sums
-    // quarters split the row on group-pair boundaries (so every batch starts on an even
-    // group); the batch count comes from the largest quarter, so it is the same for every
+    const int slot = wv / KS;     // tile group of this wave within the block
+    const int quarter = wv % KS;  // which part of the groups this wave sums
+    // parts split the row on group-pair boundaries (so every batch starts on an even
+    // group); the batch count comes from the largest part, so it is the same for every
     // wave of the block and every wave meets the per-step barrier equally often
     const int pairs = (groups + 1) >> 1;
-    const int p_begin = quarter * pairs / 4;
-    const int p_end = (quarter + 1) * pairs / 4;
+    const int p_begin = quarter * pairs / KS;
+    const int p_end = (quarter + 1) * pairs / KS;
     const int g_begin = 2 * p_begin;
     const int g_end = min(2 * p_end, groups);
-    const int nbatch = max(1, (2 * ((pairs + 3) / 4) + KB - 1) / KB);
+    const int nbatch = max(1, (2 * ((pairs + KS - 1) / KS) + KB - 1) / KB);
     const int tiles = (out_dim + 31) >> 5;
     const int tstride = gridDim.x * TPB;
 
@@ -196,6 +203,10 @@ __global__ __launch_bounds__(TPB * 256) void mfma_kernel(
     const uint4 *const xrow = lds + min(n, nb - 1) * RS + 4 * h;
     float acc[NACC];
 
+    // Whether the tile step at block base b has work: with KS > 1 the whole block walks tile
+    // steps in lockstep (one barrier per step); with KS = 1 each wave stops on its own.
+    auto more = [&](int b) { return KS == 1 ? b + slot < tiles : b < tiles; };
+
     // One unit of work: issue the next unit's loads into (nc, ns, nbv), then compute the
     // current one from (cc, sc, bc). Returns false when the block has no more tiles.
     int base = blockIdx.x * TPB;
@@ -208,7 +219,7 @@ __global__ __launch_bounds__(TPB * 256) void mfma_kernel(
         const bool last = bt + 1 == nbatch;
         const int nbase = last ? base + tstride : base;
         const int nbt = last ? 0 : bt + 1;
-        if (Q4MV_MFMA_PINGPONG && nbase < tiles) load(nbase + slot, nbt, nc, ns, nbv);
+        if (Q4MV_MFMA_PINGPONG && more(nbase)) load(nbase + slot, nbt, nc, ns, nbv);
         if (bt == 0) {
 #pragma unroll
             for (int i = 0; i < NACC; i++) acc[i] = 0.0f;
@@ -283,18 +294,23 @@ __global__ __launch_bounds__(TPB * 256) void mfma_kernel(
             }
         }
         if (last) {
-            // combine the four quarters in LDS: quarters 1..3 publish, quarter 0 adds in order
-            float *pbuf = part + (size_t)(((step & 1) * TPB + slot) * 3) * 64 * NACC;
-            if (quarter > 0) {
+            // combine the parts in LDS: parts 1..KS-1 publish, part 0 adds them in order
+            if constexpr (KS > 1) {
+                float *pbuf = part + (size_t)(((step & 1) * TPB + slot) * (KS - 1)) * 64 * NACC;
+                if (quarter > 0) {
 #pragma unroll
-                for (int i = 0; i < NACC; i++) pbuf[((quarter - 1) * NACC + i) * 64 + lane] = acc[i];
+                    for (int i = 0; i < NACC; i++)
+                        pbuf[((quarter - 1) * NACC + i) * 64 + lane] = acc[i];
+                }
+                __syncthreads();
+                if (quarter == 0) {
+#pragma unroll
+                    for (int qq = 0; qq < KS - 1; qq++)
+#pragma unroll
+                        for (int i = 0; i < NACC; i++) acc[i] += pbuf[(qq * NACC + i) * 64 + lane];
+                }
             }
-            __syncthreads();
             if (quarter == 0) {
-#pragma unroll
-                for (int qq = 0; qq < 3; qq++)
-#pragma unroll
-                    for (int i = 0; i < NACC; i++) acc[i] += pbuf[(qq * NACC + i) * 64 + lane];
                 const int orow = tile_row(tile) + n;
                 if (tile < tiles && orow < out_dim) {
 #pragma unroll
@@ -306,19 +322,19 @@ __global__ __launch_bounds__(TPB * 256) void mfma_kernel(
             }
             step++;
         }
-        if (!Q4MV_MFMA_PINGPONG && nbase < tiles) load(nbase + slot, nbt, nc, ns, nbv);
+        if (!Q4MV_MFMA_PINGPONG && more(nbase)) load(nbase + slot, nbt, nc, ns, nbv);
         base = nbase;
         bt = nbt;
-        return base < tiles;
+        return more(base);
     };
 
-    // The block walks tile steps in lockstep (one barrier per step), so its loop count is
-    // uniform: slots whose tile is past the end compute on a valid tile and store nothing.
+    // With KS > 1 the block walks tile steps in lockstep, so its loop count is uniform:
+    // slots whose tile is past the end compute on a valid tile and store nothing.
     uint4 c0[KB], c1[KB];
     uint32_t s0[KB / 2], s1[KB / 2], b0[KB / 2], b1[KB / 2];
-    if (base < tiles) load(base + slot, 0, c0, s0, b0);
+    if (more(base)) load(base + slot, 0, c0, s0, b0);
     stage();  // every wave joins the staging barrier exactly once
-    if (base < tiles) {
+    if (more(base)) {
         if constexpr (Q4MV_MFMA_PINGPONG) {
             // ping-pong between the two load buffers: no register copies per unit
             while (unit(c0, s0, b0, c1, s1, b1) && unit(c1, s1, b1, c0, s0, b0)) {
@@ -334,79 +350,85 @@ __global__ __launch_bounds__(TPB * 256) void mfma_kernel(
 typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int);
 
-template <int TPB, int KB>
+template <int WPB, int KS, int KB>
 static MfmaFn pick_mode(bool nb16, bool dword_pairs)
 {
     if (nb16)
-        return dword_pairs ? mfma_kernel<TPB, KB, true, 1, false>
-                           : mfma_kernel<TPB, KB, true, 0, false>;
-    return dword_pairs ? mfma_kernel<TPB, KB, false, 1, false>
-                       : mfma_kernel<TPB, KB, false, 0, false>;
+        return dword_pairs ? mfma_kernel<WPB, KS, KB, true, 1, false>
+                           : mfma_kernel<WPB, KS, KB, true, 0, false>;
+    return dword_pairs ? mfma_kernel<WPB, KS, KB, false, 1, false>
+                       : mfma_kernel<WPB, KS, KB, false, 0, false>;
 }
 
 // Groups per load batch: every group of a batch is computed, so the batch should divide a
-// wave's quarter of the row (at most kMaxKB groups in flight per wave).
+// wave's part of the row (at most kMaxKB groups in flight per wave).
 constexpr int kMaxKB = 12;
-static int mfma_kb(int in_dim)
+static int mfma_kb(int in_dim, int ks)
 {
     const int pairs = (in_dim / 64 + 1) / 2;
-    const int qgroups = 2 * ((pairs + 3) / 4);  // the largest quarter
+    const int qgroups = 2 * ((pairs + ks - 1) / ks);  // the largest part
     const int nbatch = (qgroups + kMaxKB - 1) / kMaxKB;
-    return 2 * ((qgroups / 2 + nbatch - 1) / nbatch);
+    const int kb = 2 * ((qgroups / 2 + nbatch - 1) / nbatch);
+    // a batch never reaches past the row (batches are shifted back to end at its last
+    // group); only a one-group row keeps kb = 2, with clamped indices
+    const int groups = in_dim / 64;
+    return kb > groups && groups >= 2 ? groups & ~1 : kb;
 }
 
-template <int TPB>
+template <int WPB, int KS>
 static MfmaFn pick_kb(int kb, bool nb16, bool dword_pairs, bool clamp)
 {
     // fewer groups than the batch (a single-group row): 2-byte scale loads, clamped indices
-    if (clamp) return nb16 ? mfma_kernel<TPB, 2, true, 0, true> : mfma_kernel<TPB, 2, false, 0, true>;
+    if (clamp)
+        return nb16 ? mfma_kernel<WPB, KS, 2, true, 0, true>
+                    : mfma_kernel<WPB, KS, 2, false, 0, true>;
     switch (kb) {
-    case 2: return pick_mode<TPB, 2>(nb16, dword_pairs);
-    case 4: return pick_mode<TPB, 4>(nb16, dword_pairs);
-    case 6: return pick_mode<TPB, 6>(nb16, dword_pairs);
-    case 8: return pick_mode<TPB, 8>(nb16, dword_pairs);
-    case 10: return pick_mode<TPB, 10>(nb16, dword_pairs);
-    default: return pick_mode<TPB, 12>(nb16, dword_pairs);
+    case 2: return pick_mode<WPB, KS, 2>(nb16, dword_pairs);
+    case 4: return pick_mode<WPB, KS, 4>(nb16, dword_pairs);
+    case 6: return pick_mode<WPB, KS, 6>(nb16, dword_pairs);
+    case 8: return pick_mode<WPB, KS, 8>(nb16, dword_pairs);
+    case 10: return pick_mode<WPB, KS, 10>(nb16, dword_pairs);
+    default: return pick_mode<WPB, KS, 12>(nb16, dword_pairs);
     }
 }
 
-int mfma_tiles_per_block(int in_dim, int nb)
+MfmaShape mfma_shape(int in_dim, int nb, long tiles)
 {
     const bool nb16 = nb > 8;
     const size_t base = mfma_lds_bytes(in_dim, nb);
-    // Two or more blocks fit on a CU: small blocks. Otherwise one block per CU holds
-    // TPB_BIG tiles if their partial sums still fit beside the activations, else one tile.
-    if (2 * (base + mfma_part_bytes(Q4MV_MFMA_TPB_SMALL, nb16)) <= kMaxLds)
-        return Q4MV_MFMA_TPB_SMALL;
-    if (base + mfma_part_bytes(Q4MV_MFMA_TPB_BIG, nb16) <= kMaxLds) return Q4MV_MFMA_TPB_BIG;
-    if (base + mfma_part_bytes(1, nb16) <= kMaxLds) return 1;
-    return 0;
+    // K-split: 1 when the tiles alone fill the GPU, else 2 or 4 waves per tile; 1 also when
+    // the partial sums would not fit beside the activations
+    const int ks = tiles < Q4MV_MFMA_KS4_BELOW ? 4 : tiles < Q4MV_MFMA_KS2_BELOW ? 2 : 1;
+    if (base + mfma_part_bytes(kMfmaWaves, ks, nb16) <= kMaxLds) return {kMfmaWaves, ks};
+    if (base <= kMaxLds) return {kMfmaWaves, 1};
+    return {0, 0};
 }
 
 hipError_t launch_mfma(const GemvArgs &a)
 {
     const int groups = a.in_dim / 64;
     const bool nb16 = a.nb > 8;
-    const int tpb = mfma_tiles_per_block(a.in_dim, a.nb);
-    if (tpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
-    const size_t lds = mfma_lds_bytes(a.in_dim, a.nb) + mfma_part_bytes(tpb, nb16);
-    const int kb = mfma_kb(a.in_dim);
+    const long tiles = (a.out_dim + 31) / 32;
+    const MfmaShape sh = mfma_shape(a.in_dim, a.nb, tiles * a.n_mat);
+    if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
+    const size_t lds = mfma_lds_bytes(a.in_dim, a.nb) + mfma_part_bytes(sh.wpb, sh.ks, nb16);
+    const int kb = mfma_kb(a.in_dim, sh.ks);
     const bool dword_pairs = groups % 2 == 0 && (uintptr_t)a.scales % 4 == 0 &&
                              (uintptr_t)a.biases % 4 == 0;
-    const bool clamp = groups < kb;  // then kb is 2 and the row has one group
-    MfmaFn fn = tpb == Q4MV_MFMA_TPB_BIG ? pick_kb<Q4MV_MFMA_TPB_BIG>(kb, nb16, dword_pairs, clamp)
-              : tpb == Q4MV_MFMA_TPB_SMALL ? pick_kb<Q4MV_MFMA_TPB_SMALL>(kb, nb16, dword_pairs, clamp)
-                                           : pick_kb<1>(kb, nb16, dword_pairs, clamp);
+    const bool clamp = groups < kb;  // only a one-group row (kb = 2)
+    MfmaFn fn = sh.ks == 1 ? pick_kb<kMfmaWaves, 1>(kb, nb16, dword_pairs, clamp)
+              : sh.ks == 2 ? pick_kb<kMfmaWaves, 2>(kb, nb16, dword_pairs, clamp)
+                           : pick_kb<kMfmaWaves, 4>(kb, nb16, dword_pairs, clamp);
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
-    const long tiles = (a.out_dim + 31) / 32;
+    const int tpb = sh.wpb / sh.ks;
     const long blocks_needed = (tiles + tpb - 1) / tpb;
     const long per_cu = std::min<long>(
         Q4MV_MFMA_BLOCKS_PER_CU,
-        resident_blocks(reinterpret_cast<const void *>(fn), tpb * 256, lds));
+        resident_blocks(reinterpret_cast<const void *>(fn), sh.wpb * 64, lds));
     const long cap = std::max(1L, (long)device_cus() * per_cu / a.n_mat);
     const long gx = std::max(1L, std::min(blocks_needed, cap));
-    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(tpb * 256), lds,
+    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(sh.wpb * 64), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
                        a.xsum, a.y, a.out_dim, a.in_dim, a.nb);

@@ -33,10 +33,27 @@ constexpr int kValuMaxNB = 8;  // nb > 8 runs as two launches over activation-ro
 #ifndef Q4MV_VALU_BLOCKS_PER_CU
 #define Q4MV_VALU_BLOCKS_PER_CU 4
 #endif
+#ifndef Q4MV_VALU1_BLOCKS_PER_CU
+#define Q4MV_VALU1_BLOCKS_PER_CU 2  // one-row kernel
+#endif
 #ifndef Q4MV_VALU_PREFETCH
 #define Q4MV_VALU_PREFETCH 0
 #endif
 constexpr bool kValuPrefetch = Q4MV_VALU_PREFETCH != 0;
+// Activations stay in registers for the whole kernel when NB * CPL is at most this.
+#ifndef Q4MV_VALU_XREG_MAX
+#define Q4MV_VALU_XREG_MAX 4
+#endif
+// Output rows per lane group in the paired kernel (2; 4 also gives the same bits).
+#ifndef Q4MV_VALU_XFIRST
+#define Q4MV_VALU_XFIRST 1
+#endif
+#ifndef Q4MV_VALU_BALANCE
+#define Q4MV_VALU_BALANCE 0
+#endif
+#ifndef Q4MV_VALU_PAIR_ROWS
+#define Q4MV_VALU_PAIR_ROWS 2
+#endif
 
 // LOG2G, CPL > 0: lane-group size and chunks per lane fixed at compile time (the common row
 // lengths); LOG2G = -1, CPL = 0: both taken at run time (any in_dim).
@@ -49,44 +66,60 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
 {
     const int log2g = LOG2G >= 0 ? LOG2G : log2g_rt;
     extern __shared__ uint4 lds[];
-    constexpr bool XREG = CPL > 0 && NB * CPL <= 4;
+    constexpr bool XREG = CPL > 0 && NB * CPL <= Q4MV_VALU_XREG_MAX;
     const int m = blockIdx.y;
     const int C = in_dim >> 5;
     const int groups = in_dim >> 6;
     const int words8 = in_dim >> 3;  // uint2 units (4 halves) per activation row
 
-    // Stage activation rows r0 .. r0+NB-1 of matrix m (pair layout + scaled sums). Called
-    // after each wave has issued its first weight loads, so the two latencies overlap.
-    auto stage = [&]() {
-        const size_t xrow0 = (size_t)m * nb_total + r0;
-        const uint2 *xe_m = xe + xrow0 * words8;
-        const uint2 *xo_m = xo + xrow0 * words8;
-        const float *xsum_m = xsum + xrow0 * C;
-        float *xsw = reinterpret_cast<float *>(lds + NB * C * 4);
-        const int units = NB * C * 4;  // 16-byte pair units; NB*C chunk sums
-        // each round issues all of its loads before any LDS write: one memory round trip
-        for (int base = threadIdx.x; base < units; base += 4 * kValuThreads) {
-            uint2 e[4], o[4];
+    // Stage activation rows r0 .. r0+NB-1 of matrix m (pair layout + scaled sums) in LDS.
+    // stage_load issues one round of loads into registers and stage_store writes them, so a
+    // wave can put its first weight loads between the two and the latencies overlap.
+    const size_t xrow0 = (size_t)m * nb_total + r0;
+    const uint2 *xe_m = xe + xrow0 * words8;
+    const uint2 *xo_m = xo + xrow0 * words8;
+    const float *xsum_m = xsum + xrow0 * C;
+    float *xsw = reinterpret_cast<float *>(lds + NB * C * 4);
+    const int units = NB * C * 4;  // 16-byte pair units; NB*C chunk sums
+    struct XStage { uint2 e[4], o[4]; float sv; };
+    auto stage_load = [&](int base, XStage &st) {
+        // indices clamped: rounds past the end read valid data that stage_store drops
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int u = min(base + i * kValuThreads, units - 1);
+        for (int i = 0; i < 4; i++) {
+            const int u = min(base + i * kValuThreads, units - 1);
+            const int r = u / (C * 4), cj = u - r * (C * 4);
+            st.e[i] = xe_m[(size_t)r * words8 + cj];
+            st.o[i] = xo_m[(size_t)r * words8 + cj];
+        }
+        const int us = (base - threadIdx.x) / 4 + threadIdx.x;  // chunk-sum index
+        st.sv = xsum_m[min(us, NB * C - 1)];
+    };
+    auto stage_store = [&](int base, const XStage &st) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int u = base + i * kValuThreads;
+            if (u < units) {
                 const int r = u / (C * 4), cj = u - r * (C * 4);
-                e[i] = xe_m[(size_t)r * words8 + cj];
-                o[i] = xo_m[(size_t)r * words8 + cj];
+                lds[x_unit(r, cj >> 2, cj & 3, C)] = make_pairs(st.e[i], st.o[i]);
             }
-            const int us = (base - threadIdx.x) / 4 + threadIdx.x;  // chunk-sum index
-            const float sv = xsum_m[min(us, NB * C - 1)];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int u = base + i * kValuThreads;
-                if (u < units) {
-                    const int r = u / (C * 4), cj = u - r * (C * 4);
-                    lds[x_unit(r, cj >> 2, cj & 3, C)] = make_pairs(e[i], o[i]);
-                }
-            }
-            if (us < NB * C) xsw[us] = sv * kTwoM24;
+        }
+        const int us = (base - threadIdx.x) / 4 + threadIdx.x;
+        if (us < NB * C) xsw[us] = st.sv * kTwoM24;
+    };
+    // the remaining rounds and the barrier; the first round's loads are in st0
+    auto stage_finish = [&](const XStage &st0) {
+        stage_store(threadIdx.x, st0);
+        for (int base = threadIdx.x + 4 * kValuThreads; base < units; base += 4 * kValuThreads) {
+            XStage st;
+            stage_load(base, st);
+            stage_store(base, st);
         }
         __syncthreads();
+    };
+    auto stage = [&]() {
+        XStage st0;
+        stage_load(threadIdx.x, st0);
+        stage_finish(st0);
     };
     const float *xs = reinterpret_cast<const float *>(lds + NB * C * 4);
 
@@ -126,32 +159,33 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
         // ---- fully unrolled chunk loop
         uint4 cc[ROWS][CPL];
         uint32_t scb[ROWS][CPL], bcb[ROWS][CPL];
+        // Loads are issued in the order compute() consumes them (chunk-major, then row), and
+        // scales are converted where they are used, so the compiler's waits on the load
+        // counter are progressive: a wave starts on its first chunk while the rest is still
+        // in flight.
         auto load = [&](int ws, uint4 (&cw)[ROWS][CPL], uint32_t (&sv)[ROWS][CPL],
                         uint32_t (&bv)[ROWS][CPL]) {
+            const uint4 *wr[ROWS];
+            const uint16_t *sr[ROWS], *br[ROWS];
 #pragma unroll
             for (int t = 0; t < ROWS; t++) {
                 const int row = min(ws * rows_per_wave + grp * ROWS + t, out_dim - 1);
-                const uint4 *wr = w_m + (size_t)row * C;
-                const uint16_t *sr = s_m + (size_t)row * groups;
-                const uint16_t *br = b_m + (size_t)row * groups;
+                wr[t] = w_m + (size_t)row * C;
+                sr[t] = s_m + (size_t)row * groups;
+                br[t] = b_m + (size_t)row * groups;
+            }
 #pragma unroll
-                for (int k = 0; k < CPL; k++) {
-                    const int c = j + (k << log2g);
-                    cw[t][k] = wr[c];
-                    sv[t][k] = sr[c >> 1];
-                    bv[t][k] = br[c >> 1];
+            for (int k = 0; k < CPL; k++) {
+                const int c = j + (k << log2g);
+#pragma unroll
+                for (int t = 0; t < ROWS; t++) {
+                    cw[t][k] = wr[t][c];
+                    sv[t][k] = sr[t][c >> 1];
+                    bv[t][k] = br[t][c >> 1];
                 }
             }
         };
         auto compute = [&](int ws) {
-            float sc[ROWS][CPL], bc[ROWS][CPL];
-#pragma unroll
-            for (int t = 0; t < ROWS; t++)
-#pragma unroll
-                for (int k = 0; k < CPL; k++) {
-                    sc[t][k] = bf16_to_f32(scb[t][k]);
-                    bc[t][k] = bf16_to_f32(bcb[t][k]);
-                }
             float acc[ROWS][NB];
 #pragma unroll
             for (int t = 0; t < ROWS; t++)
@@ -190,17 +224,21 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                     }
 #pragma unroll
                     for (int t = 0; t < ROWS; t++) {
-                        float ae = 0.0f, ao = 0.0f;
+                        float ae = dot2_first(h[t][0][0], xp[0].x);
+                        float ao = dot2_first(h[t][0][1], xp[0].y);
+                        ae = dot2(h[t][0][2], xp[0].z, ae);
+                        ao = dot2(h[t][0][3], xp[0].w, ao);
 #pragma unroll
-                        for (int J = 0; J < 4; J++) {
+                        for (int J = 1; J < 4; J++) {
                             ae = dot2(h[t][J][0], xp[J].x, ae);
                             ao = dot2(h[t][J][1], xp[J].y, ao);
                             ae = dot2(h[t][J][2], xp[J].z, ae);
                             ao = dot2(h[t][J][3], xp[J].w, ao);
                         }
                         const float qd = __builtin_fmaf(ao, 0.0625f, ae);
-                        acc[t][r] = __builtin_fmaf(sc[t][k], qd,
-                                                   __builtin_fmaf(bc[t][k], xsv, acc[t][r]));
+                        acc[t][r] = __builtin_fmaf(bf16_to_f32(scb[t][k]), qd,
+                                                   __builtin_fmaf(bf16_to_f32(bcb[t][k]), xsv,
+                                                                  acc[t][r]));
                     }
                 }
             }
@@ -243,8 +281,17 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                 compute(ws);
             }
         } else {
+#if Q4MV_VALU_XFIRST
+            // activations first (small, mostly cache hits), then the first step's weights:
+            // the staging only waits for its own loads
+            XStage st0;
+            stage_load(threadIdx.x, st0);
+            if (ws < wave_steps) load(ws, cc, scb, bcb);
+            stage_finish(st0);
+#else
             if (ws < wave_steps) load(ws, cc, scb, bcb);  // first step's weights, before staging
             stage();
+#endif
             load_xreg();
             for (bool first = true; ws < wave_steps; ws += wstride, first = false) {
                 // Compiler fence: keeps the per-step LDS activation reads inside the loop
@@ -296,9 +343,12 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                         for (int t = 0; t < ROWS; t++) {
                             const uint32_t wd[4] = {cc[t][kk].x, cc[t][kk].y, cc[t][kk].z,
                                                     cc[t][kk].w};
-                            float ae = 0.0f, ao = 0.0f;
+                            float ae = dot2_first(wd[0] & 0x000F000Fu, xp[0].x);
+                            float ao = dot2_first(wd[0] & 0x00F000F0u, xp[0].y);
+                            ae = dot2((wd[0] >> 8) & 0x000F000Fu, xp[0].z, ae);
+                            ao = dot2((wd[0] >> 8) & 0x00F000F0u, xp[0].w, ao);
 #pragma unroll
-                            for (int J = 0; J < 4; J++) {
+                            for (int J = 1; J < 4; J++) {
                                 const uint32_t w8 = wd[J] >> 8;
                                 ae = dot2(wd[J] & 0x000F000Fu, xp[J].x, ae);
                                 ao = dot2(wd[J] & 0x00F000F0u, xp[J].y, ao);
@@ -370,7 +420,8 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const int log2g = valu_log2g(a.in_dim);
     const int C = a.in_dim / 32;
     const int cpl = C >> log2g;
-    ValuFn fn = rows == 2 ? pick_nb<2>(nbp, log2g, cpl) : pick_nb<1>(nbp, log2g, cpl);
+    if (rows == 2) rows = Q4MV_VALU_PAIR_ROWS;
+    ValuFn fn = rows == 1 ? pick_nb<1>(nbp, log2g, cpl) : pick_nb<Q4MV_VALU_PAIR_ROWS>(nbp, log2g, cpl);
     const size_t lds = (size_t)nbp * C * 64 + (size_t)nbp * C * 4;
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
@@ -378,11 +429,17 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const long wave_steps = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
     const long blocks_needed = (wave_steps + 3) / 4;
     // persistent blocks: enough to fill every CU a few times over, shared by the matrices
-    const long per_cu = std::min<long>(Q4MV_VALU_BLOCKS_PER_CU,
+    const long per_cu = std::min<long>(rows == 1 ? Q4MV_VALU1_BLOCKS_PER_CU : Q4MV_VALU_BLOCKS_PER_CU,
                                        resident_blocks(reinterpret_cast<const void *>(fn),
                                                        kValuThreads, lds));
     const long cap = std::max(1L, (long)device_cus() * per_cu / a.n_mat);
-    const long gx = std::max(1L, std::min(blocks_needed, cap));
+    long gx = std::max(1L, std::min(blocks_needed, cap));
+#if Q4MV_VALU_BALANCE
+    // every wave takes the same number of row steps: the fewest blocks that keep the
+    // number of rounds of the full grid (no partly filled last round)
+    const long rounds = (wave_steps + 4 * gx - 1) / (4 * gx);
+    gx = std::max(1L, (wave_steps + 4 * rounds - 1) / (4 * rounds));
+#endif
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(kValuThreads), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),

@@ -227,15 +227,28 @@ def _read_csv_rows(run_dir, suffix):
     return rows
 
 
-def summarize_trace(run_dir, out, cmd):
+def summarize_trace(run_dir, out, cmd, bench_log=None):
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run, plus the GEMV kernel
+    duration bench.py measured with HIP events in the same run (from its JSON line)."""
     rows = _read_csv_rows(run_dir, "kernel_stats.csv")
     if not rows:
         raise SystemExit(f"no kernel_stats.csv under {run_dir}")
     lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}",
              "# columns: calls, total_ns, average_ns, min_ns, max_ns, percent, kernel"]
     for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+        name = r.get("Name", "")
+        name = name[:name.index("(")] if "(" in name and not name.startswith("_Z") else name
         lines.append(f"{r.get('Calls')}, {r.get('TotalDurationNs')}, {r.get('AverageNs')}, "
-                     f"{r.get('MinNs')}, {r.get('MaxNs')}, {r.get('Percentage')}, {r.get('Name')}")
+                     f"{r.get('MinNs')}, {r.get('MaxNs')}, {r.get('Percentage')}, {name}")
+    if bench_log:
+        for line in open(bench_log):
+            if line.startswith("{"):
+                res = json.loads(line)
+                gemv = [r for r in rows if res["roofline"]["kernel"] in r.get("Name", "")]
+                lines.append(f"# bench.py in the same run: {res['roofline']['kernel']} "
+                             f"{res['roofline']['kernel_us']} us per launch (HIP events); "
+                             f"rocprofv3 average "
+                             f"{float(gemv[0]['AverageNs']) / 1e3 if gemv else float('nan'):.3f} us")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -328,9 +341,10 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="")
+    ap.add_argument("--bench-log", help="bench.py output of the profiled run")
     args = ap.parse_args()
     if args.summarize_trace:
-        return summarize_trace(args.summarize_trace, args.out, args.cmd)
+        return summarize_trace(args.summarize_trace, args.out, args.cmd, args.bench_log)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.workload, args.nb, args.cmd, args.out)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

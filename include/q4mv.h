@@ -123,9 +123,10 @@ int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               int out_dim, int in_dim, int nb, int path, void *stream);
 
 /* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
-   (two_row = 1) takes for this shape; a negative status if the shape is invalid. For small
-   nb, q4mv runs the two-row kernel whenever out_dim is even (the results are bitwise the
-   same as the one-row kernel's), and nb > 3 runs on the MFMA kernel. */
+   (two_row = 1) takes for this shape; a negative status if the shape is invalid. nb > 3
+   runs on the MFMA kernel. Below that q4mv_2row takes the two-row kernel, and q4mv the
+   one-row kernel for nb = 1 and the two-row kernel for nb = 2, 3 when out_dim is even (the
+   two VALU kernels give bitwise the same result). */
 int q4mv_auto_path(int in_dim, int nb, int two_row, int out_dim);
 
 /* Static English text for a status code. */

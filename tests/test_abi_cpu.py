@@ -97,9 +97,10 @@ def test_pack_validation(L):
 
 
 def test_auto_path(L):
-    assert L.q4mv_auto_path(2560, 1, 0, 9) == 1    # odd out_dim: one-row kernel
-    assert L.q4mv_auto_path(2560, 1, 0, 10) == 2   # even out_dim: two-row kernel
-    assert L.q4mv_auto_path(640, 1, 1, 2560) == 2
+    assert L.q4mv_auto_path(2560, 1, 0, 10) == 1   # one activation row: one-row kernel
+    assert L.q4mv_auto_path(2560, 2, 0, 9) == 1    # odd out_dim: one-row kernel
+    assert L.q4mv_auto_path(2560, 2, 0, 10) == 2   # even out_dim: two-row kernel
+    assert L.q4mv_auto_path(640, 1, 1, 2560) == 2  # q4mv_2row: two-row kernel
     assert L.q4mv_auto_path(2560, 3, 0, 2560) == 2
     assert L.q4mv_auto_path(2560, 4, 0, 2560) == 3
     assert L.q4mv_auto_path(2560, 16, 1, 2560) == 3
