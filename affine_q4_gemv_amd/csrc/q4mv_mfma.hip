@@ -39,6 +39,10 @@
 #ifndef Q4MV_MFMA_APREFETCH
 #define Q4MV_MFMA_APREFETCH 0
 #endif
+// Non-temporal weight loads (each byte is used once).
+#ifndef Q4MV_MFMA_NT
+#define Q4MV_MFMA_NT 0
+#endif
 #ifndef Q4MV_MFMA_BLOCKS_PER_CU
 #define Q4MV_MFMA_BLOCKS_PER_CU 4
 #endif
@@ -183,14 +187,28 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
         for (int kk = 0; kk < KB; kk++) {
             // only rows with fewer groups than KB need the clamp (then gl = 0)
             const int k = CLAMP ? min(kk, groups - 1) : kk;
+#if Q4MV_MFMA_NT
+            {
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 v =
+                    __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wt + lw + 2 * k));
+                cw[kk] = uint4{v[0], v[1], v[2], v[3]};
+            }
+#else
             cw[kk] = wt[lw + 2 * k];
+#endif
         }
 #pragma unroll
         for (int kp = 0; kp < KB / 2; kp++) {
             const int k0 = CLAMP ? min(2 * kp, groups - 1) : 2 * kp;
             if constexpr (SMODE == 1) {  // gl and k0 are even: an aligned dword
+#if Q4MV_MFMA_NT
+                sv[kp] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(st + ls + k0));
+                bv[kp] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(bt_ + ls + k0));
+#else
                 sv[kp] = *reinterpret_cast<const uint32_t *>(st + ls + k0);
                 bv[kp] = *reinterpret_cast<const uint32_t *>(bt_ + ls + k0);
+#endif
             } else {
                 const int k1 = CLAMP ? min(k0 + 1, groups - 1) : k0 + 1;
                 sv[kp] = (uint32_t)st[ls + k0] | ((uint32_t)st[ls + k1] << 16);

@@ -42,9 +42,13 @@ constexpr int kValuMaxNB = 8;  // nb > 8 runs as two launches over activation-ro
 constexpr bool kValuPrefetch = Q4MV_VALU_PREFETCH != 0;
 // Activations stay in registers for the whole kernel when NB * CPL is at most this.
 #ifndef Q4MV_VALU_XREG_MAX
-#define Q4MV_VALU_XREG_MAX 4
+#define Q4MV_VALU_XREG_MAX 5
 #endif
 // Output rows per lane group in the paired kernel (2; 4 also gives the same bits).
+// Weights are read with non-temporal loads (each byte is used once; measured faster).
+#ifndef Q4MV_VALU_NT
+#define Q4MV_VALU_NT 1
+#endif
 #ifndef Q4MV_VALU_XFIRST
 #define Q4MV_VALU_XFIRST 1
 #endif
@@ -179,9 +183,21 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                 const int c = j + (k << log2g);
 #pragma unroll
                 for (int t = 0; t < ROWS; t++) {
+#if Q4MV_VALU_NT
+                    // streamed once: non-temporal loads (no reuse to keep in the caches)
+                    {
+                        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                        const u32x4 v = __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4 *>(wr[t] + c));
+                        cw[t][k] = uint4{v[0], v[1], v[2], v[3]};
+                    }
+                    sv[t][k] = __builtin_nontemporal_load(sr[t] + (c >> 1));
+                    bv[t][k] = __builtin_nontemporal_load(br[t] + (c >> 1));
+#else
                     cw[t][k] = wr[t][c];
                     sv[t][k] = sr[t][c >> 1];
                     bv[t][k] = br[t][c >> 1];
+#endif
                 }
             }
         };
