@@ -10,15 +10,16 @@ namespace q4mv_impl {
 // (measured crossover on MI355X).
 constexpr int kValuAutoMaxNB = 3;
 
-// The automatic choice: MFMA for larger batches. Below that, q4mv_2row runs the two-row
+// The automatic choice: MFMA for larger batches when its LDS footprint fits (else the VALU
+// kernels, which handle every nb). Below that, q4mv_2row runs the two-row
 // kernel; q4mv runs one activation row on the one-row kernel (on MI355X it is as fast or
 // faster at every measured shape, the 640-wide expert down projection included) and 2..3
 // rows on the two-row kernel when out_dim is even. The one-row and two-row kernels give
 // bitwise the same result, so q4mv and q4mv_2row agree whichever they take.
 int auto_path(int in_dim, int nb, bool two_row, int out_dim)
 {
-    (void)in_dim;
-    if (nb > kValuAutoMaxNB) return kMfma;
+    // the MFMA kernel's LDS footprint does not depend on the tile count for the fit itself
+    if (nb > kValuAutoMaxNB && mfma_shape(in_dim, nb, 1).wpb != 0) return kMfma;
     if (two_row) return kValu2;
     return nb > 1 && out_dim % 2 == 0 ? kValu2 : kValu1;
 }

@@ -114,9 +114,11 @@ int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
  *   2: VALU kernel, two rows per lane group (q4mv_2row; out_dim must be even),
  *   3: MFMA kernel (32x32x16 f16 matrix cores; activation rows padded to 32).
  * Same arguments, layouts and errors as q4mv, plus PATH for an unknown path, and SHAPE when
- * path 3 is asked for a shape whose activations and sums do not fit in LDS
- * (about 2*nb*in_dim + in_dim bytes; only nb <= 2 with very long rows). For testing and
- * measurement of every kernel at every nb.
+ * path 3 is asked for a shape whose staged activations and sums
+ * (nb*(in_dim/8+1)*16 + in_dim bytes) plus an 18 KB scratch do not fit in the 160 KB of LDS
+ * (in_dim >= 48512, 29120, 20800 for nb = 1, 2, 3, and in_dim >= 16192 for nb = 4; the
+ * automatic dispatch never sends those shapes there). For testing and measurement of every
+ * kernel at every nb.
  */
 int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
@@ -124,7 +126,8 @@ int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
 
 /* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
    (two_row = 1) takes for this shape; a negative status if the shape is invalid. nb > 3
-   runs on the MFMA kernel. Below that q4mv_2row takes the two-row kernel, and q4mv the
+   runs on the MFMA kernel when its LDS footprint fits (see q4mv_path), else on the VALU
+   kernels. Below that q4mv_2row takes the two-row kernel, and q4mv the
    one-row kernel for nb = 1 and the two-row kernel for nb = 2, 3 when out_dim is even (the
    two VALU kernels give bitwise the same result). */
 int q4mv_auto_path(int in_dim, int nb, int two_row, int out_dim);
