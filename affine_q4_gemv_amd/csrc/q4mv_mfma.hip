@@ -42,6 +42,15 @@
 #ifndef Q4MV_MFMA_KS_BIG
 #define Q4MV_MFMA_KS_BIG 2
 #endif
+#ifndef Q4MV_MFMA_NT
+#define Q4MV_MFMA_NT 1
+#endif
+#ifndef Q4MV_MFMA_SB_COMPACT
+#define Q4MV_MFMA_SB_COMPACT 0
+#endif
+#ifndef Q4MV_MFMA_BALANCE
+#define Q4MV_MFMA_BALANCE 0
+#endif
 #ifndef Q4MV_MFMA_BLOCKS_PER_CU
 #define Q4MV_MFMA_BLOCKS_PER_CU 4
 #endif
@@ -54,6 +63,9 @@ constexpr int kMfmaWaves = 8;
 // 2 x 32 rows x 8 B (in 16-byte units).
 constexpr int kScratchUnits = 32 * 8 + 32;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// A unit's scales and biases in flight: two dwords (one 8-byte load per lane) or four
+// 2-byte values (compact loads).
+struct SbRegs { uint32_t v[4]; };
 
 // WPB: waves per block. KS: waves per tile (K-split). NB16: activation rows 8..15 are live
 // (nb > 8). SB8: scales and biases of a quad are one aligned 8-byte load (groups % 4 == 0
@@ -167,36 +179,64 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const int lr8 = lane >> 3, lc = lane & 7;
     const int sbrow = narrow ? min(lane & 31, out_dim - 1) : (lane & 31);
     const uint16_t *const sb_m = lane < 32 ? s_m : b_m;
-    auto load = [&](int tile, int qd, u32x4 (&cw)[4], uint2 &sb) {
+    auto load = [&](int tile, int qd, u32x4 (&cw)[4], SbRegs &sb) {
         const int trow = tile_row(tile);
         const int chunk = min(8 * qd + lc, C - 1);
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = narrow ? min(8 * r + lr8, out_dim - 1) : 8 * r + lr8;
+#if Q4MV_MFMA_NT
+            // each 128-byte line is read whole, once: non-temporal
+            cw[r] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(w_m) + (size_t)(trow + row) * C + chunk);
+#else
             cw[r] = reinterpret_cast<const u32x4 *>(w_m)[(size_t)(trow + row) * C + chunk];
+#endif
         }
+#if Q4MV_MFMA_SB_COMPACT
+        // four 2-byte loads per lane: load i covers the scales (i < 2) or biases of rows
+        // 16*(i&1) .. +15, four consecutive lanes reading one row's four groups
+        const int g = min(4 * qd + (lane & 3), groups - 1);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = 16 * (i & 1) + (lane >> 2);
+            const int rr = narrow ? min(row, out_dim - 1) : row;
+            sb.v[i] = (i < 2 ? s_m : b_m)[(size_t)(trow + rr) * groups + g];
+        }
+#else
         const uint16_t *srow = sb_m + (size_t)(trow + sbrow) * groups;
         if constexpr (SB8) {
-            sb = *reinterpret_cast<const uint2 *>(srow + 4 * qd);
+            const uint2 v = *reinterpret_cast<const uint2 *>(srow + 4 * qd);
+            sb.v[0] = v.x;
+            sb.v[1] = v.y;
         } else {
             uint32_t v[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) v[i] = srow[min(4 * qd + i, groups - 1)];
-            sb = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+            sb.v[0] = v[0] | (v[1] << 16);
+            sb.v[1] = v[2] | (v[3] << 16);
         }
+#endif
     };
     // This wave's scratch: codes of row r, chunk slot c at r*8 + (c ^ (r & 7)) (the XOR
     // keeps both the row-major writes and the MFMA-layout reads free of bank conflicts),
     // then scales of rows 0..31 and biases of rows 0..31 as 8-byte entries.
     uint4 *const scratch = scratch_all + wv * kScratchUnits;
     uint2 *const sbs = reinterpret_cast<uint2 *>(scratch + 32 * 8);
-    auto put = [&](const u32x4 (&cw)[4], const uint2 &sb) {
+    auto put = [&](const u32x4 (&cw)[4], const SbRegs &sb) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = 8 * r + lr8;
             reinterpret_cast<u32x4 *>(scratch)[row * 8 + (lc ^ (row & 7))] = cw[r];
         }
-        sbs[lane] = sb;
+#if Q4MV_MFMA_SB_COMPACT
+        uint16_t *const sbs16 = reinterpret_cast<uint16_t *>(sbs);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            sbs16[((i >> 1) * 32 + 16 * (i & 1) + (lane >> 2)) * 4 + (lane & 3)] = (uint16_t)sb.v[i];
+#else
+        sbs[lane] = uint2{sb.v[0], sb.v[1]};
+#endif
     };
 
     // this lane's activation row in LDS (row nb - 1 past nb), offset to its chunk parity
@@ -211,19 +251,32 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     int step = 0;
     auto unit_quad = [&](int u) { return min(q_begin + u, quads - 1); };
 
-    u32x4 cc[4];
-    uint2 sb;
-    if (more(base)) load(base + slot, unit_quad(0), cc, sb);
+    // Loads run two units ahead: (abase, aui) is the unit the next load fetches, and the
+    // two register sets alternate (the loop is unrolled by two so each set is static).
+    int abase = base, aui = 0;
+    auto advance = [&](int &b, int &u) {
+        if (u + 1 == nunit) {
+            u = 0;
+            b += tstride;
+        } else {
+            u++;
+        }
+    };
+    u32x4 c0[4], c1[4];
+    SbRegs s0, s1;
+    if (more(abase)) load(abase + slot, unit_quad(aui), c0, s0);
+    advance(abase, aui);
+    if (more(abase)) load(abase + slot, unit_quad(aui), c1, s1);
+    advance(abase, aui);
     stage();  // every wave joins the staging barrier exactly once
     if (!more(base)) return;
-    for (;;) {
+    auto step_unit = [&](u32x4 (&cc)[4], SbRegs &sb) {
         const int tile = base + slot;
         const int qd = q_begin + ui;  // may be past this wave's part: then all masked
         const bool last = ui + 1 == nunit;
-        const int nbase = last ? base + tstride : base;
-        const int nui = last ? 0 : ui + 1;
         put(cc, sb);  // waits for this unit's loads
-        if (more(nbase)) load(nbase + slot, unit_quad(nui), cc, sb);
+        if (more(abase)) load(abase + slot, unit_quad(aui), cc, sb);
+        advance(abase, aui);
         if (ui == 0) {
 #pragma unroll
             for (int i = 0; i < NACC; i++) acc[i] = 0.0f;
@@ -295,9 +348,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
             }
             step++;
         }
-        base = nbase;
-        ui = nui;
-        if (!more(base)) break;
+        advance(base, ui);
+        return more(base);
+    };
+    while (step_unit(c0, s0) && step_unit(c1, s1)) {
     }
 }
 
@@ -360,7 +414,13 @@ hipError_t launch_mfma(const GemvArgs &a)
         Q4MV_MFMA_BLOCKS_PER_CU,
         resident_blocks(reinterpret_cast<const void *>(fn), sh.wpb * 64, lds));
     const long cap = std::max(1L, (long)device_cus() * std::max(1L, per_cu) / a.n_mat);
-    const long gx = std::max(1L, std::min(blocks_needed, cap));
+    long gx = std::max(1L, std::min(blocks_needed, cap));
+#if Q4MV_MFMA_BALANCE
+    // the fewest blocks that keep the number of tile rounds: every tile group gets the same
+    // number of tiles (no partly filled last round)
+    const long rounds = (tiles + gx * tpb - 1) / (gx * tpb);
+    gx = std::max(1L, ((tiles + rounds - 1) / rounds + tpb - 1) / tpb);
+#endif
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(sh.wpb * 64), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
