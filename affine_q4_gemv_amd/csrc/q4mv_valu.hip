@@ -46,6 +46,12 @@ constexpr bool kValuPrefetch = Q4MV_VALU_PREFETCH != 0;
 #endif
 // Output rows per lane group in the paired kernel (2; 4 also gives the same bits).
 // Weights are read with non-temporal loads (each byte is used once; measured faster).
+// With activations in registers, load them straight from device memory (no LDS staging).
+// Measured slower on MI355X (LM head NB=1 43 us against 36.5 us), so off.
+#ifndef Q4MV_VALU_XDIRECT
+#define Q4MV_VALU_XDIRECT 0
+#endif
+constexpr bool kValuXDirect = Q4MV_VALU_XDIRECT != 0;
 #ifndef Q4MV_VALU_NT
 #define Q4MV_VALU_NT 1
 #endif
@@ -144,6 +150,25 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     // activations in registers for the whole kernel when they fit
     uint4 xr[XREG ? CPL : 1][XREG ? NB : 1][4];
     float xsr[XREG ? CPL : 1][XREG ? NB : 1];
+    // Activations straight from device memory into registers (no LDS, no barrier): the
+    // lane's chunks of every activation row, converted to the pair layout.
+    auto load_xreg_direct = [&]() {
+        if constexpr (XREG) {
+            const size_t xrow0 = (size_t)m * nb_total + r0;
+#pragma unroll
+            for (int k = 0; k < CPL; k++) {
+                const int c = j + (k << log2g);
+#pragma unroll
+                for (int r = 0; r < NB; r++) {
+                    const uint2 *xe_r = xe + (xrow0 + r) * words8 + 4 * c;
+                    const uint2 *xo_r = xo + (xrow0 + r) * words8 + 4 * c;
+#pragma unroll
+                    for (int J = 0; J < 4; J++) xr[k][r][J] = make_pairs(xe_r[J], xo_r[J]);
+                    xsr[k][r] = xsum[(xrow0 + r) * C + c] * kTwoM24;
+                }
+            }
+        }
+    };
     auto load_xreg = [&]() {
         if constexpr (XREG) {
 #pragma unroll
@@ -296,6 +321,16 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                 if (ws + wstride < wave_steps) load(ws + wstride, cn, sn, bn);
                 compute(ws);
             }
+        } else if constexpr (XREG && kValuXDirect) {
+            // activations first (few bytes, cache hits after the first wave), then the first
+            // step's weights; no LDS and no barrier
+            load_xreg_direct();
+            if (ws < wave_steps) load(ws, cc, scb, bcb);
+            for (bool first = true; ws < wave_steps; ws += wstride, first = false) {
+                asm volatile("" ::: "memory");
+                if (!first) load(ws, cc, scb, bcb);
+                compute(ws);
+            }
         } else {
 #if Q4MV_VALU_XFIRST
             // activations first (small, mostly cache hits), then the first step's weights:
@@ -405,6 +440,16 @@ typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const 
     X(6, 2) /* 4096 */ X(5, 5) /* 5120 */ X(6, 3) /* 6144 */ X(5, 7) /* 7168 */               \
     X(6, 4) /* 8192 */ X(6, 7) /* 14336 */
 
+// Whether (log2 G, CPL) is one of the specialised row lengths.
+static bool valu_specialised(int log2g, int cpl)
+{
+#define Q4MV_IS(L, K) \
+    if (log2g == L && cpl == K) return true;
+    Q4MV_VALU_SHAPES(Q4MV_IS)
+#undef Q4MV_IS
+    return false;
+}
+
 template <int NB, int ROWS>
 static ValuFn pick_shape(int log2g, int cpl)
 {
@@ -438,7 +483,11 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const int cpl = C >> log2g;
     if (rows == 2) rows = Q4MV_VALU_PAIR_ROWS;
     ValuFn fn = rows == 1 ? pick_nb<1>(nbp, log2g, cpl) : pick_nb<Q4MV_VALU_PAIR_ROWS>(nbp, log2g, cpl);
-    const size_t lds = (size_t)nbp * C * 64 + (size_t)nbp * C * 4;
+    // activations straight into registers need no LDS (same rule as the kernel's XREG; the
+    // generic kernel and NB > 4 always stage)
+    const bool xdirect = kValuXDirect && nbp <= 4 && valu_specialised(log2g, cpl) &&
+                         nbp * cpl <= Q4MV_VALU_XREG_MAX;
+    const size_t lds = xdirect ? 0 : (size_t)nbp * C * 64 + (size_t)nbp * C * 4;
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
     const int rows_per_wave = (64 >> log2g) * rows;
