@@ -46,19 +46,23 @@ def lib():
             from . import build as _build
             _build.build()
         L = ctypes.CDLL(LIB_PATH)
-        p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        p, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
         L.q4mv_pack_codes.argtypes = [p, p, i64, p]
         L.q4mv_prepare_x.argtypes = [p, i32, i32, p, p, p, p]
         gemv = [p, p, p, p, p, p, p, i32, i32, i32, i32]
         L.q4mv.argtypes = gemv + [p]
         L.q4mv_2row.argtypes = gemv + [p]
         L.q4mv_path.argtypes = gemv + [i32, p]
+        L.q4mv_silu.argtypes = gemv + [f32, p]
+        L.q4mv_path_silu.argtypes = gemv + [f32, i32, p]
+        L.q4mv_swiglu_prep.argtypes = [p, i32, i32, p, p, p, p]
         L.q4mv_auto_path.argtypes = [i32, i32, i32, i32]
         L.q4mv_status_str.argtypes = [i32]
         L.q4mv_status_str.restype = ctypes.c_char_p
         L.q4mv_version.argtypes = []
         for fn in ("q4mv_pack_codes", "q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_path",
-                   "q4mv_auto_path", "q4mv_version"):
+                   "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_auto_path",
+                   "q4mv_version"):
             getattr(L, fn).restype = i32
         _lib = L
     return _lib
@@ -133,7 +137,7 @@ def q4mv_prepare_x(x, xe=None, xo=None, xsum=None, stream=None):
     return xe, xo, xsum
 
 
-def _gemv(fn_name, w, scales, biases, xe, xo, xsum, nb, y, stream, path=None):
+def _gemv(fn_name, w, scales, biases, xe, xo, xsum, nb, y, stream, path=None, div=None):
     torch = _torch()
     if w.dim() != 3:
         raise ValueError("w: expected [n_mat, out_dim, in_dim/8]")
@@ -150,6 +154,8 @@ def _gemv(fn_name, w, scales, biases, xe, xo, xsum, nb, y, stream, path=None):
     _need(y, torch.float32, (n_mat, nb, out_dim), "y")
     args = [w.data_ptr(), scales.data_ptr(), biases.data_ptr(), xe.data_ptr(), xo.data_ptr(),
             xsum.data_ptr(), y.data_ptr(), n_mat, out_dim, in_dim, nb]
+    if div is not None:
+        args.append(float(div))
     if path is not None:
         args.append(int(path))
     args.append(_stream(w, stream))
@@ -170,6 +176,39 @@ def q4mv_2row(w, scales, biases, xe, xo, xsum, nb, y=None, stream=None):
 def q4mv_path(w, scales, biases, xe, xo, xsum, nb, path, y=None, stream=None):
     """:func:`q4mv` with an explicit kernel (PATH_VALU, PATH_VALU_2ROW, PATH_MFMA)."""
     return _gemv("q4mv_path", w, scales, biases, xe, xo, xsum, nb, y, stream, path=path)
+
+
+def q4mv_silu(w, scales, biases, xe, xo, xsum, nb, div, y=None, stream=None):
+    """silu(q4mv(...) / div), fused into the GEMV's store."""
+    return _gemv("q4mv_silu", w, scales, biases, xe, xo, xsum, nb, y, stream, div=div)
+
+
+def q4mv_path_silu(w, scales, biases, xe, xo, xsum, nb, div, path, y=None, stream=None):
+    """:func:`q4mv_silu` with an explicit kernel path."""
+    return _gemv("q4mv_path_silu", w, scales, biases, xe, xo, xsum, nb, y, stream, path=path,
+                 div=div)
+
+
+def q4mv_swiglu_prep(gu, xe=None, xo=None, xsum=None, stream=None):
+    """gu f32 [n_rows, 2*inter] (gate | up) -> prep of h = silu(gate)*up:
+    (xe, xo f16 [n_rows, inter/2], xsum f32 [n_rows, inter/32])."""
+    torch = _torch()
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu: expected [n_rows, 2*inter]")
+    n, k2 = gu.shape
+    k = k2 // 2
+    _need(gu, torch.float32, (n, k2), "gu")
+    dev = gu.device
+    xe = torch.empty((n, k // 2), dtype=torch.float16, device=dev) if xe is None else xe
+    xo = torch.empty((n, k // 2), dtype=torch.float16, device=dev) if xo is None else xo
+    xsum = torch.empty((n, k // 32), dtype=torch.float32, device=dev) if xsum is None else xsum
+    _need(xe, torch.float16, (n, k // 2), "xe")
+    _need(xo, torch.float16, (n, k // 2), "xo")
+    _need(xsum, torch.float32, (n, k // 32), "xsum")
+    _check("q4mv_swiglu_prep", lib().q4mv_swiglu_prep(gu.data_ptr(), n, k, xe.data_ptr(),
+                                                       xo.data_ptr(), xsum.data_ptr(),
+                                                       _stream(gu, stream)))
+    return xe, xo, xsum
 
 
 def q4mv_auto_path(in_dim: int, nb: int, two_row: bool = False, out_dim: int = 2) -> int:

@@ -2,6 +2,8 @@
 #include "../../include/q4mv.h"
 #include "q4mv_internal.h"
 
+#include <cmath>
+
 #include <mutex>
 
 namespace q4mv_impl {
@@ -107,7 +109,8 @@ static int check_gemv(const uint32_t *w, const uint16_t *scales, const uint16_t 
 
 static int run_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
                     const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
-                    int out_dim, int in_dim, int nb, int path, void *stream)
+                    int out_dim, int in_dim, int nb, int path, void *stream,
+                    float epi_div = 0.0f)
 {
     int st = check_gemv(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb);
     if (st != Q4MV_OK) return st;
@@ -116,7 +119,7 @@ static int run_path(const uint32_t *w, const uint16_t *scales, const uint16_t *b
     if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
     if (path == kMfma && mfma_shape(in_dim, nb, (long)n_mat * ((out_dim + 31) / 32)).wpb == 0)
         return Q4MV_ERR_SHAPE;
-    GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
+    GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb, epi_div,
                static_cast<hipStream_t>(stream)};
     hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
     return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
@@ -150,6 +153,40 @@ int q4mv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, cons
 {
     return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
                     auto_path(in_dim, nb, false, out_dim), stream);
+}
+
+int q4mv_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+              const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+              int out_dim, int in_dim, int nb, float div, void *stream)
+{
+    int st = check_gemv(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb);
+    if (st != Q4MV_OK) return st;
+    if (!(div != 0.0f) || !std::isfinite(div)) return Q4MV_ERR_VALUE;
+    return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb,
+                    auto_path(in_dim, nb, false, out_dim), stream, div);
+}
+
+int q4mv_path_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                   const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+                   int out_dim, int in_dim, int nb, float div, int path, void *stream)
+{
+    int st = check_gemv(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb);
+    if (st != Q4MV_OK) return st;
+    if (!(div != 0.0f) || !std::isfinite(div)) return Q4MV_ERR_VALUE;
+    return run_path(w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb, path, stream,
+                    div);
+}
+
+int q4mv_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo, float *xsum,
+                     void *stream)
+{
+    if (!gu || !xe || !xo || !xsum) return Q4MV_ERR_NULL;
+    if (n_rows < 1 || inter < 64 || inter % 64 != 0) return Q4MV_ERR_SHAPE;
+    if (!aligned(gu, 8) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(xsum, 4))
+        return Q4MV_ERR_ALIGN;
+    hipError_t e =
+        launch_swiglu_prep(gu, n_rows, inter, xe, xo, xsum, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
 }
 
 int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
@@ -190,10 +227,11 @@ const char *q4mv_status_str(int status)
     case Q4MV_ERR_ALIGN: return "a pointer is not aligned as required";
     case Q4MV_ERR_LAUNCH: return "the HIP kernel launch failed";
     case Q4MV_ERR_PATH: return "unknown kernel path";
+    case Q4MV_ERR_VALUE: return "an argument value is invalid (div must be finite and nonzero)";
     default: return "unknown status";
     }
 }
 
-int q4mv_version(void) { return 100; }
+int q4mv_version(void) { return 200; }
 
 }  // extern "C"

@@ -23,6 +23,16 @@ constexpr float kTwoM24 = 5.9604644775390625e-08f;
 // bf16 bit pattern (in the low 16 bits) -> f32: the bits are the high half of the f32.
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
+// Output epilogue of the GEMV: silu(v / div) = t / (1 + e^-t) with t = v / div (the gated
+// bottleneck of fn_qmv_silu_b, Constant BATCH_MSL page); div == 0 stores v unchanged. div is a
+// kernel argument, so the branch is uniform.
+__device__ __forceinline__ float gemv_epilogue(float v, float div)
+{
+    if (div == 0.0f) return v;
+    const float t = v / div;
+    return t / (1.0f + expf(-t));
+}
+
 // a.lo*b.lo + a.hi*b.hi + c with f16 inputs and f32 accumulation (v_dot2c_f32_f16).
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {

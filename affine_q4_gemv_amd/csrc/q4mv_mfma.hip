@@ -75,7 +75,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
-    int out_dim, int in_dim, int nb)
+    int out_dim, int in_dim, int nb, float epi_div)
 {
     constexpr int TH = WPB * 64;
     constexpr int TPB = WPB / KS;  // tile groups per block
@@ -342,7 +342,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 #pragma unroll
                     for (int i = 0; i < NACC; i++) {
                         const int r = 8 * (i / 4) + 4 * h + (i % 4);
-                        if (r < nb) y_m[(size_t)r * out_dim + orow] = acc[i] * kTwo24;
+                        if (r < nb)
+                            y_m[(size_t)r * out_dim + orow] = gemv_epilogue(acc[i] * kTwo24, epi_div);
                     }
                 }
             }
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 }
 
 typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
-                       const uint2 *, const float *, float *, int, int, int);
+                       const uint2 *, const float *, float *, int, int, int, float);
 
 template <int WPB, int KS>
 static MfmaFn pick(bool nb16, bool sb8)
@@ -424,7 +425,7 @@ hipError_t launch_mfma(const GemvArgs &a)
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(sh.wpb * 64), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
-                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb);
+                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, a.epi_div);
     return hipGetLastError();
 }
 

@@ -46,6 +46,46 @@ __global__ __launch_bounds__(256) void prep_kernel(const float2 *__restrict__ x,
     if ((threadIdx.x & 15) == 0) xsum[i >> 4] = s;
 }
 
+// SwiGLU activation fused with the prep of the down projection's input (fn_moe_act_b on the
+// Constant BATCH_MSL page): row n of gu holds gate[0..inter) then up[0..inter); h = silu(gate)
+// * up in f32 becomes the f16 even/odd streams of an inter-wide activation row, and each
+// 32-column chunk gets the sum of its f16-rounded values. One thread per (row, pair k).
+__global__ __launch_bounds__(256) void swiglu_prep_kernel(const float2 *__restrict__ gu,
+                                                          _Float16 *__restrict__ xe,
+                                                          _Float16 *__restrict__ xo,
+                                                          float *__restrict__ xsum,
+                                                          int64_t n_pairs, int half_inter)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // n_pairs and half_inter are multiples of 32: a 16-lane row is entirely in range or out
+    if (i >= n_pairs) return;
+    const int64_t row = i / half_inter, k = i - row * half_inter;
+    const float2 g = gu[row * (2 * half_inter) + k];               // gate[2k], gate[2k+1]
+    const float2 u = gu[row * (2 * half_inter) + half_inter + k];  // up[2k], up[2k+1]
+    const float he = g.x / (1.0f + expf(-g.x)) * u.x;
+    const float ho = g.y / (1.0f + expf(-g.y)) * u.y;
+    const _Float16 a = (_Float16)he, b = (_Float16)ho;
+    xe[i] = a;
+    xo[i] = b;
+    float s = (float)a + (float)b;
+    s += dpp<0xB1>(s);
+    s += dpp<0x4E>(s);
+    s += dpp<0x141>(s);
+    s += dpp<0x140>(s);
+    if ((threadIdx.x & 15) == 0) xsum[i >> 4] = s;
+}
+
+hipError_t launch_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo,
+                              float *xsum, hipStream_t s)
+{
+    const int64_t n_pairs = (int64_t)n_rows * (inter / 2);
+    const int64_t blocks = (n_pairs + 255) / 256;
+    hipLaunchKernelGGL(swiglu_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float2 *>(gu), static_cast<_Float16 *>(xe),
+                       static_cast<_Float16 *>(xo), xsum, n_pairs, inter / 2);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s)
 {
     const int64_t n_words = n_codes / 8;

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
-    int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt)
+    int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt, float epi_div)
 {
     const int log2g = LOG2G >= 0 ? LOG2G : log2g_rt;
     extern __shared__ uint4 lds[];
@@ -295,7 +295,8 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                     if (row < out_dim) {
 #pragma unroll
                         for (int r = 0; r < NB; r++)
-                            y_m[(size_t)r * out_dim + row] = acc[t][r] * kTwo24;
+                            y_m[(size_t)r * out_dim + row] =
+                                gemv_epilogue(acc[t][r] * kTwo24, epi_div);
                     }
                 }
             }
@@ -420,7 +421,8 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
 #pragma unroll
                 for (int r = 0; r < NB; r++) {
                     const float v = group_sum(acc[t][r], log2g);
-                    if (j == 0 && row < out_dim) y_m[(size_t)r * out_dim + row] = v * kTwo24;
+                    if (j == 0 && row < out_dim)
+                        y_m[(size_t)r * out_dim + row] = gemv_epilogue(v * kTwo24, epi_div);
                 }
             }
         }
@@ -431,7 +433,8 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
 // host side
 
 typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
-                       const uint2 *, const float *, float *, int, int, int, int, int, int);
+                       const uint2 *, const float *, float *, int, int, int, int, int, int,
+                       float);
 
 // (log2 G, CPL) of the specialised row lengths: in_dim = 32 * CPL << log2G.
 #define Q4MV_VALU_SHAPES(X)                                                                   \
@@ -508,7 +511,7 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(kValuThreads), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
-                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, r0, log2g, cpl);
+                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, r0, log2g, cpl, a.epi_div);
     return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ def load_traffic(workload, nb, kernel):
 class Problem:
     """Device buffers of one workload: R rotated weight copies, activations and outputs."""
 
-    def __init__(self, name, nb, rotate=True):
+    def __init__(self, name, nb, rotate=True, silu_div=None):
         import numpy as np
         import torch
 
@@ -77,6 +77,7 @@ class Problem:
         import workloads
 
         self.q4, self.torch = q4, torch
+        self.silu_div = silu_div
         c = workloads.make_case(name, nb=nb)
         self.name = name
         self.n_mat, self.out_dim, self.in_dim, self.nb = c["n_mat"], c["out_dim"], c["in_dim"], nb
@@ -119,8 +120,12 @@ class Problem:
 
     def gemv(self, i):
         k = i % self.R
-        self.q4.q4mv(self.w[k], self.s[k], self.b[k], self.xe, self.xo, self.xsum, self.nb,
-                     y=self.y)
+        if self.silu_div is not None:
+            self.q4.q4mv_silu(self.w[k], self.s[k], self.b[k], self.xe, self.xo, self.xsum,
+                              self.nb, self.silu_div, y=self.y)
+        else:
+            self.q4.q4mv(self.w[k], self.s[k], self.b[k], self.xe, self.xo, self.xsum, self.nb,
+                         y=self.y)
 
     def _graph(self, body, n):
         """Capture n iterations of body(i) in a HIP graph (after one eager warm-up)."""
@@ -194,6 +199,64 @@ class Problem:
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
+
+
+class MoeChain(Problem):
+    """The expert MLP of the MoE workload: 8 experts, hidden 2560, intermediate 640, NB=4.
+    One step = stacked gate|up GEMV + fused SwiGLU prep + down GEMV (three launches)."""
+
+    def __init__(self, n_mat=8, hidden=2560, inter=640, nb=4):
+        import numpy as np
+        import torch
+
+        import affine_q4_gemv_amd as q4
+        import workloads
+        self.q4, self.torch = q4, torch
+        self.silu_div = None
+        dev = torch.device("cuda:0")
+        up = workloads.make_shape(n_mat, 2 * inter, hidden, nb, seed=21)
+        dn = workloads.make_shape(n_mat, hidden, inter, nb, seed=22, x_scale=0.5)
+
+        def put(c):
+            w = q4.q4mv_pack_codes(torch.from_numpy(c["codes"]).to(dev))
+            s = torch.from_numpy(c["scales"].view(np.int16)).to(dev).view(torch.bfloat16)
+            b = torch.from_numpy(c["biases"].view(np.int16)).to(dev).view(torch.bfloat16)
+            return w, s, b
+        self.weight_bytes = (workloads.weight_bytes(n_mat, 2 * inter, hidden)
+                             + workloads.weight_bytes(n_mat, hidden, inter))
+        self.R = max(1, math.ceil(ROTATE_BYTES / self.weight_bytes))
+        w1, s1, b1 = put(up)
+        w2, s2, b2 = put(dn)
+        self.sets = [(w1, s1, b1, w2, s2, b2)] + [
+            tuple(t.clone() for t in (w1, s1, b1, w2, s2, b2)) for _ in range(self.R - 1)]
+        x = torch.from_numpy(up["x"].reshape(n_mat * nb, hidden)).to(dev)
+        self.xe, self.xo, self.xsum = q4.q4mv_prepare_x(x)
+        self.gu = torch.empty((n_mat, nb, 2 * inter), dtype=torch.float32, device=dev)
+        self.xe2 = torch.empty((n_mat * nb, inter // 2), dtype=torch.float16, device=dev)
+        self.xo2 = torch.empty_like(self.xe2)
+        self.xsum2 = torch.empty((n_mat * nb, inter // 32), dtype=torch.float32, device=dev)
+        self.y = torch.empty((n_mat, nb, hidden), dtype=torch.float32, device=dev)
+        self.nb, self.n_mat, self.inter = nb, n_mat, inter
+        torch.cuda.synchronize()
+
+    def prep(self):
+        pass
+
+    def gemv(self, i):
+        w1, s1, b1, w2, s2, b2 = self.sets[i % self.R]
+        q4 = self.q4
+        q4.q4mv(w1, s1, b1, self.xe, self.xo, self.xsum, self.nb, y=self.gu)
+        q4.q4mv_swiglu_prep(self.gu.view(self.n_mat * self.nb, 2 * self.inter), self.xe2,
+                            self.xo2, self.xsum2)
+        q4.q4mv(w2, s2, b2, self.xe2, self.xo2, self.xsum2, self.nb, y=self.y)
+
+    def check_graph_output(self):
+        torch = self.torch
+        got = self.y.clone()
+        self.gemv(0)
+        torch.cuda.synchronize()
+        if not torch.equal(got, self.y):
+            raise RuntimeError("graph replay output differs from the eager call")
 
 
 def cpu_baseline(name, nb, budget_s=10.0):
@@ -415,6 +478,23 @@ def main():
                           "path": p.path})
             del p
             torch.cuda.empty_cache()
+        # fused epilogues: the silu(y / div) store, and the expert MLP chain
+        p = Problem("lm_head", 1, silu_div=2.0)
+        ms = p.time_kernel(200)
+        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+        sweep.append({"workload": "lm_head", "nb": 1, "epilogue": "silu(y/2)",
+                      "kernel_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
+                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1), "path": p.path})
+        del p
+        p = MoeChain()
+        ms = p.time_kernel(200)
+        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+        sweep.append({"workload": "moe_mlp 8x(2560->2x640->2560)", "nb": 4,
+                      "launches": "gate|up GEMV + SwiGLU prep + down GEMV",
+                      "step_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
+                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
+        del p
+        torch.cuda.empty_cache()
         result["sweep"] = sweep
 
     if not args.no_cpu:

@@ -37,7 +37,8 @@ enum {
     Q4MV_ERR_ODD_ROWS = -3, /* q4mv_2row with an odd out_dim */
     Q4MV_ERR_ALIGN = -4,    /* a pointer is not aligned as required */
     Q4MV_ERR_LAUNCH = -5,   /* the HIP launch reported an error */
-    Q4MV_ERR_PATH = -6      /* q4mv_path: unknown kernel path */
+    Q4MV_ERR_PATH = -6,     /* q4mv_path: unknown kernel path */
+    Q4MV_ERR_VALUE = -7     /* q4mv_silu: div is zero or not finite */
 };
 
 /* Largest activation batch accepted (rows per matrix). */
@@ -123,6 +124,38 @@ int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
 int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
               int out_dim, int in_dim, int nb, int path, void *stream);
+
+/*
+ * q4mv_silu -- q4mv with the output passed through silu(y / div):
+ *   y[m][r][o] = t / (1 + exp(-t)),  t = (the q4mv result) / div
+ * the gated-residual bottleneck of fn_qmv_silu_b on the Constant BATCH_MSL page, fused into
+ * the GEMV's store (one launch, no extra pass over y). t is formed in f32 by a division and
+ * exp is the device library's single-precision exp. Same arguments, layouts, kernels and
+ * errors as q4mv, plus VALUE when div is 0 or not finite.
+ */
+int q4mv_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+              const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+              int out_dim, int in_dim, int nb, float div, void *stream);
+
+/* q4mv_silu with an explicit kernel path (as q4mv_path). */
+int q4mv_path_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                   const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+                   int out_dim, int in_dim, int nb, float div, int path, void *stream);
+
+/*
+ * q4mv_swiglu_prep -- the SwiGLU activation of an expert MLP fused with the activation prep
+ * of its down projection (fn_moe_act_b on the Constant BATCH_MSL page, whose input is the
+ * stacked gate/up output of fn_moe_gate_up_b):
+ *   gu   : f32 [n_rows][2*inter]   row n = gate[0..inter) then up[0..inter), e.g. the y of a
+ *          q4mv over the stacked gate+up weights (out_dim = 2*inter; n_rows = n_mat*nb)
+ *   h[n][j] = silu(gate[n][j]) * up[n][j], computed in f32 (silu(g) = g / (1 + exp(-g)))
+ *   xe, xo, xsum : as q4mv_prepare_x would produce for x = h (in_dim = inter): the f16
+ *          even/odd streams of h and the f32 sums of each 32 f16-rounded values.
+ * Errors: NULL pointer; n_rows < 1, inter < 64 or inter % 64 != 0 (SHAPE); gu not 8-byte,
+ * xe or xo not 16-byte, xsum not 4-byte aligned (ALIGN).
+ */
+int q4mv_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo, float *xsum,
+                     void *stream);
 
 /* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
    (two_row = 1) takes for this shape; a negative status if the shape is invalid. nb > 3

@@ -13,6 +13,9 @@ never imports it.
   contributes one sum. The sum is taken over the f16-rounded values, as ``fn_moe_act_b``
   does (``fn_norm_prep_b`` sums the f32 values instead; the f16 reading keeps the bias term
   and the code term on the same x).
+* :func:`silu`, :func:`gemv_silu`, :func:`swiglu` -- the fused epilogues of the same page:
+  ``fn_qmv_silu_b`` stores silu(y / div), and ``fn_moe_act_b`` forms silu(gate) * up from the
+  stacked gate/up output before the down projection's prep.
 """
 from __future__ import annotations
 
@@ -139,3 +142,37 @@ def xsum_error_bound(x):
         xh = np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)
     a = np.abs(xh).reshape(xh.shape[0], xh.shape[1] // 32, 32).sum(axis=2)
     return 31.0 * 2.0 ** -24 * a
+
+
+def silu(t):
+    """silu(t) = t / (1 + e^-t) in double (the output of fn_qmv_silu_b and the gate of
+    fn_moe_act_b on the Constant BATCH_MSL page). Written as t * e^t / (1 + e^t) for t < 0 so
+    that e^-t never overflows."""
+    t = np.asarray(t, dtype=np.float64)
+    out = np.empty_like(t)
+    pos = t >= 0
+    out[pos] = t[pos] / (1.0 + np.exp(-t[pos]))
+    e = np.exp(t[~pos])
+    out[~pos] = t[~pos] * e / (1.0 + e)
+    return out
+
+
+# max |d silu / dt| (attained near t = 2.4): an error e in t moves silu(t) by at most 1.1 e
+SILU_LIPSCHITZ = 1.1
+
+
+def gemv_silu(codes, scales, biases, x, div, nthreads: int | None = None):
+    """silu(y / div) for the GEMV y (fn_qmv_silu_b), and the propagated per-element bound:
+    an error within bound in y moves the output by at most SILU_LIPSCHITZ * bound / |div|."""
+    y, bound = gemv(codes, scales, biases, x, nthreads=nthreads)
+    return silu(y / div), SILU_LIPSCHITZ * bound / abs(div)
+
+
+def swiglu(gu):
+    """h = silu(gate) * up for rows of gu = [gate | up] (f64 [n][2*inter] -> [n][inter]), the
+    activation of fn_moe_act_b on the Constant BATCH_MSL page."""
+    gu = np.asarray(gu, dtype=np.float64)
+    if gu.ndim != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be [n_rows][2*inter]")
+    k = gu.shape[1] // 2
+    return silu(gu[:, :k]) * gu[:, k:]

@@ -9,7 +9,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "q4mv.h")
 
-OK, ENULL, ESHAPE, EODD, EALIGN, ELAUNCH, EPATH = 0, -1, -2, -3, -4, -5, -6
+OK, ENULL, ESHAPE, EODD, EALIGN, ELAUNCH, EPATH, EVALUE = 0, -1, -2, -3, -4, -5, -6, -7
 A = 0x10000  # a 16-byte aligned fake address: validation fails before anything reads it
 
 
@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     fns = declared_functions()
     for name in ("q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_pack_codes", "q4mv_path",
-                 "q4mv_auto_path", "q4mv_status_str", "q4mv_version"):
+                 "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_auto_path",
+                 "q4mv_status_str", "q4mv_version"):
         assert name in fns
 
 
@@ -39,10 +40,10 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_status_strings(L):
     import affine_q4_gemv_amd as q
-    for st in (OK, ENULL, ESHAPE, EODD, EALIGN, ELAUNCH, EPATH):
+    for st in (OK, ENULL, ESHAPE, EODD, EALIGN, ELAUNCH, EPATH, EVALUE):
         assert q.status_str(st) and q.status_str(st) != "unknown status"
     assert q.status_str(12345) == "unknown status"
-    assert L.q4mv_version() >= 100
+    assert L.q4mv_version() >= 200
 
 
 def gemv_args(**kw):
@@ -115,3 +116,28 @@ def test_binding_rejects_cpu_tensors():
     import affine_q4_gemv_amd as q
     with pytest.raises(ValueError):
         q.q4mv_prepare_x(torch.zeros(1, 128))
+
+
+def test_silu_validation(L):
+    for fn, extra in (("q4mv_silu", []), ("q4mv_path_silu", [0])):
+        f = getattr(L, fn)
+        for div in (0.0, float("inf"), float("-inf"), float("nan")):
+            assert f(*gemv_args(), div, *extra, None) == EVALUE, (fn, div)
+        # the GEMV's own checks come first
+        assert f(*gemv_args(w=None), 2.0, *extra, None) == ENULL
+        assert f(*gemv_args(ind=96), 2.0, *extra, None) == ESHAPE
+        assert f(*gemv_args(w=A + 4), 2.0, *extra, None) == EALIGN
+    assert L.q4mv_path_silu(*gemv_args(), 2.0, 7, None) == EPATH
+    assert L.q4mv_path_silu(*gemv_args(out=7), 2.0, 2, None) == EODD
+
+
+def test_swiglu_prep_validation(L):
+    f = L.q4mv_swiglu_prep
+    assert f(None, 1, 640, A, A, A, None) == ENULL
+    assert f(A, 1, 640, A, None, A, None) == ENULL
+    assert f(A, 0, 640, A, A, A, None) == ESHAPE
+    assert f(A, 1, 32, A, A, A, None) == ESHAPE
+    assert f(A, 1, 96, A, A, A, None) == ESHAPE
+    assert f(A + 4, 1, 640, A, A, A, None) == EALIGN
+    assert f(A, 1, 640, A + 8, A, A, None) == EALIGN
+    assert f(A, 1, 640, A, A, A + 2, None) == EALIGN

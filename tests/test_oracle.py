@@ -321,3 +321,58 @@ def test_mutants_are_caught(tmp_path):
         gemv = _load_variant(str(so))
         failed = [p.__name__ for p in PINS if not p(gemv)]
         assert failed, f"mutant {name} passed every pin"
+
+
+# --- fused epilogues (Constant BATCH_MSL page, fn_qmv_silu_b and fn_moe_act_b) -------------
+
+def test_silu_identities(oracle_lib):
+    oracle = oracle_lib
+    # silu(t) - silu(-t) = t exactly, and silu(t) = (t/2)(1 + tanh(t/2)): the second form uses
+    # tanh instead of exp, so it checks the exp-based oracle against independent arithmetic
+    t = np.concatenate([np.linspace(-60, 60, 2401), [0.0, 1e-300, -1e-300, 700.0, -700.0]])
+    s = oracle.silu(t)
+    np.testing.assert_allclose(s - oracle.silu(-t), t, rtol=1e-15, atol=1e-300)
+    # (the tanh form cancels for t << 0, so there it is compared in absolute terms)
+    th = 0.5 * t * (1.0 + np.tanh(0.5 * t))
+    near = t > -5
+    np.testing.assert_allclose(s[near], th[near], rtol=1e-13, atol=1e-300)
+    assert np.all(np.abs(s - th) <= 1e-14 * np.abs(t) + 1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert np.all(np.isfinite(s))
+
+
+def test_silu_lipschitz_constant(oracle_lib):
+    oracle = oracle_lib
+    # the bound used for the epilogue: max |silu'| over a fine grid stays below 1.1
+    t = np.linspace(-20, 20, 400001)
+    d = np.gradient(oracle.silu(t), t)
+    assert d.max() < oracle.SILU_LIPSCHITZ and d.max() > 1.09
+
+
+def test_gemv_silu_sign_symmetry(oracle_lib):
+    oracle = oracle_lib
+    # the GEMV is linear in x: y(-x) = -y(x), so silu(y(-x) / -div) = silu(y(x) / div), and
+    # the odd identity gives silu(y/div) - silu(-y/div) = y / div
+    c = workloads.make_shape(2, 40, 256, 3, seed=11)
+    a, _ = oracle.gemv_silu(c["codes"], c["scales"], c["biases"], c["x"], 3.0)
+    b, _ = oracle.gemv_silu(c["codes"], c["scales"], c["biases"], -c["x"], -3.0)
+    np.testing.assert_array_equal(a, b)
+    m, _ = oracle.gemv_silu(c["codes"], c["scales"], c["biases"], -c["x"], 3.0)
+    y, _ = oracle.gemv(c["codes"], c["scales"], c["biases"], c["x"])
+    np.testing.assert_allclose(a - m, y / 3.0, rtol=1e-12, atol=1e-12)
+
+
+def test_swiglu_closed_forms(oracle_lib):
+    oracle = oracle_lib
+    rng = np.random.default_rng(5)
+    g = rng.normal(size=(3, 64)) * 4
+    u = rng.normal(size=(3, 64))
+    h = oracle.swiglu(np.concatenate([g, u], axis=1))
+    # odd identity in the gate, linearity in up, and the saturated gate
+    h_neg = oracle.swiglu(np.concatenate([-g, u], axis=1))
+    np.testing.assert_allclose(h - h_neg, g * u, rtol=1e-13, atol=1e-13)
+    h2 = oracle.swiglu(np.concatenate([g, 2 * u], axis=1))
+    np.testing.assert_array_equal(h2, 2 * h)
+    big = oracle.swiglu(np.concatenate([np.full((1, 64), 50.0), u[:1]], axis=1))
+    np.testing.assert_allclose(big, 50.0 * u[:1], rtol=1e-15)
+    assert np.all(oracle.swiglu(np.concatenate([np.zeros((1, 64)), u[:1]], axis=1)) == 0)
