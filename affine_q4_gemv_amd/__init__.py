@@ -56,12 +56,14 @@ def lib():
         L.q4mv_silu.argtypes = gemv + [f32, p]
         L.q4mv_path_silu.argtypes = gemv + [f32, i32, p]
         L.q4mv_swiglu_prep.argtypes = [p, i32, i32, p, p, p, p]
+        L.q4mv_quantize.argtypes = [p, p, p, p, i64, i32, p]
         L.q4mv_auto_path.argtypes = [i32, i32, i32, i32]
         L.q4mv_status_str.argtypes = [i32]
         L.q4mv_status_str.restype = ctypes.c_char_p
         L.q4mv_version.argtypes = []
         for fn in ("q4mv_pack_codes", "q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_path",
-                   "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_auto_path",
+                   "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_quantize",
+                   "q4mv_auto_path",
                    "q4mv_version"):
             getattr(L, fn).restype = i32
         _lib = L
@@ -187,6 +189,24 @@ def q4mv_path_silu(w, scales, biases, xe, xo, xsum, nb, div, path, y=None, strea
     """:func:`q4mv_silu` with an explicit kernel path."""
     return _gemv("q4mv_path_silu", w, scales, biases, xe, xo, xsum, nb, y, stream, path=path,
                  div=div)
+
+
+def q4mv_quantize(wf, stream=None):
+    """Dense f32 weights [..., in_dim] -> (w int32 [..., in_dim/8], scales, biases bfloat16
+    [..., in_dim/64]): affine-Q4 with per-64 min/max (see include/q4mv.h)."""
+    torch = _torch()
+    if wf.dtype != torch.float32 or not wf.is_cuda or not wf.is_contiguous():
+        raise ValueError("wf: contiguous float32 GPU tensor expected")
+    in_dim = wf.shape[-1]
+    lead = tuple(wf.shape[:-1])
+    n_rows = wf.numel() // in_dim if in_dim else 0
+    w = torch.empty(lead + (in_dim // 8,), dtype=torch.int32, device=wf.device)
+    s = torch.empty(lead + (in_dim // 64,), dtype=torch.bfloat16, device=wf.device)
+    b = torch.empty_like(s)
+    _check("q4mv_quantize", lib().q4mv_quantize(wf.data_ptr(), w.data_ptr(), s.data_ptr(),
+                                                 b.data_ptr(), n_rows, in_dim,
+                                                 _stream(wf, stream)))
+    return w, s, b
 
 
 def q4mv_swiglu_prep(gu, xe=None, xo=None, xsum=None, stream=None):

@@ -177,6 +177,19 @@ int q4mv_path_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *bi
                     div);
 }
 
+int q4mv_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint16_t *biases,
+                  int64_t n_rows, int in_dim, void *stream)
+{
+    if (!wf || !w || !scales || !biases) return Q4MV_ERR_NULL;
+    if (n_rows < 1 || in_dim < 64 || in_dim % 64 != 0 || n_rows * (in_dim / 64) > (1LL << 40))
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(wf, 16) || !aligned(w, 4) || !aligned(scales, 2) || !aligned(biases, 2))
+        return Q4MV_ERR_ALIGN;
+    hipError_t e =
+        launch_quantize(wf, w, scales, biases, n_rows, in_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
 int q4mv_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo, float *xsum,
                      void *stream)
 {

@@ -35,6 +35,8 @@ inline int valu_log2g(int in_dim)
 int auto_path(int in_dim, int nb, bool two_row, int out_dim);
 
 hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s);
+hipError_t launch_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint16_t *biases,
+                           int64_t n_rows, int in_dim, hipStream_t s);
 hipError_t launch_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo,
                               float *xsum, hipStream_t s);
 hipError_t launch_prep(const float *x, int n_rows, int in_dim, void *xe, void *xo, float *xsum,

@@ -86,6 +86,73 @@ hipError_t launch_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, 
     return hipGetLastError();
 }
 
+// Affine-Q4 quantiser for dense rows, one 16-lane row per 64-wide group. The
+// steps are those of the affine 5-bit host codec on the memra-engine qwen4exp_gpu.rs page
+// (host_quant_q5_row), with 16 levels and a 64-wide group: min and max of the group,
+// d = (max - min) / 15, id = 1 / d (0 when d is 0 or id is not finite),
+// q = clamp(round_half_even((w - min) * id), 0, 15), all in f32 with correctly rounded
+// division; scale = bf16(d), bias = bf16(min), round to nearest even. Codes go straight into
+// the packed layout q4mv reads (code i of a word at bits [4i, 4i+4)).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float row_min(float v)
+{
+    v = fminf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fminf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fminf(v, dpp<0x141>(v));  // row_half_mirror
+    return fminf(v, dpp<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row_max(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    return fmaxf(v, dpp<0x140>(v));
+}
+
+// One 16-lane DPP row per group: lane j of the row holds columns 4j .. 4j+3.
+__global__ __launch_bounds__(256) void quantize_kernel(const float4 *__restrict__ wf,
+                                                       uint32_t *__restrict__ w,
+                                                       uint16_t *__restrict__ scales,
+                                                       uint16_t *__restrict__ biases,
+                                                       int64_t n_groups)
+{
+    const int64_t grp = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    if (grp >= n_groups) return;  // whole 16-lane rows: the DPP below stays inside live rows
+    const int j = threadIdx.x & 15;
+    const float4 v = wf[grp * 16 + j];
+    const float mn = row_min(fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+    const float mx = row_max(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    const float d = __fdiv_rn(mx - mn, 15.0f);
+    float id = d != 0.0f ? __frcp_rn(d) : 0.0f;
+    if (!isfinite(id)) id = 0.0f;
+    auto code = [&](float x) {
+        return (uint32_t)fminf(fmaxf(rintf((x - mn) * id), 0.0f), 15.0f);
+    };
+    const uint32_t h = code(v.x) | (code(v.y) << 4) | (code(v.z) << 8) | (code(v.w) << 12);
+    // lanes 2i and 2i+1 make word i of the group (codes 8i .. 8i+7)
+    const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0xB1, 0xF, 0xF, true);
+    if ((j & 1) == 0) w[grp * 8 + (j >> 1)] = h | (other << 16);
+    if (j == 0) {
+        scales[grp] = (uint16_t)f32_to_bf16_rne(d);
+        biases[grp] = (uint16_t)f32_to_bf16_rne(mn);
+    }
+}
+
+hipError_t launch_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint16_t *biases,
+                           int64_t n_rows, int in_dim, hipStream_t s)
+{
+    const int64_t n_groups = n_rows * (in_dim / 64);
+    const int64_t blocks = (n_groups + 15) / 16;  // 16 groups of 16 lanes per block
+    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(wf), w, scales, biases, n_groups);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s)
 {
     const int64_t n_words = n_codes / 8;

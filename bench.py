@@ -486,6 +486,25 @@ def main():
                       "kernel_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
                       "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1), "path": p.path})
         del p
+        # the quantiser (off the GEMV path): dense f32 LM-head weights -> packed affine-Q4
+        wf = torch.randn(151936, 2560, device="cuda") * 0.02
+        q4 = __import__("affine_q4_gemv_amd")
+        q4.q4mv_quantize(wf)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(10):
+            q4.q4mv_quantize(wf)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / 10
+        moved = wf.numel() * 4 + wf.numel() // 2 + wf.numel() // 64 * 4
+        sweep.append({"workload": "quantize lm_head f32 151936x2560 -> affine-Q4",
+                      "kernel_us": round(ms * 1e3, 1),
+                      "GBps_read_plus_written": round(moved / (ms * 1e-3) / 1e9, 1),
+                      "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)})
+        del wf
+        torch.cuda.empty_cache()
         p = MoeChain()
         ms = p.time_kernel(200)
         gbps = p.weight_bytes / (ms * 1e-3) / 1e9

@@ -62,6 +62,26 @@ enum {
 int q4mv_pack_codes(const uint8_t *codes, uint32_t *w, int64_t n_codes, void *stream);
 
 /*
+ * q4mv_quantize -- affine-Q4 quantisation of dense f32 weights into the layout q4mv reads.
+ *
+ * For each row and each 64-wide group, the steps of the affine 5-bit host codec
+ * (host_quant_q5_row on the memra-engine qwen4exp_gpu.rs page) with 16 levels:
+ *   mn = min, mx = max of the group;  d = (mx - mn) / 15;  id = 1 / d (0 when d == 0 or
+ *   1/d is not finite);  q = clamp(round_half_even((w - mn) * id), 0, 15)
+ * computed in f32 (correctly rounded division), scale = bf16(d) and bias = bf16(mn) (round to
+ * nearest even). The dequantised weight scale*q + bias is then within d/2 of w plus the bf16
+ * rounding of scale and bias.
+ *   wf     : f32 [n_rows][in_dim]        (n_rows = n_mat * out_dim; rows are independent)
+ *   w      : u32 [n_rows][in_dim/8]      packed codes (q4mv_pack_codes layout)
+ *   scales, biases : u16 [n_rows][in_dim/64] bf16 bit patterns
+ * Inputs must be finite (other values give unspecified codes, never a fault).
+ * Errors: NULL pointer; n_rows < 1, in_dim < 64 or in_dim % 64 != 0 (SHAPE); wf not
+ * 16-byte, w not 4-byte, scales/biases not 2-byte aligned (ALIGN).
+ */
+int q4mv_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint16_t *biases,
+                  int64_t n_rows, int in_dim, void *stream);
+
+/*
  * q4mv_prepare_x -- activation prep for the GEMV.
  *
  * Constant BATCH_MSL page, fn_norm_prep_b (its prep half) and fn_moe_act_b: x is split into

@@ -176,3 +176,33 @@ def swiglu(gu):
         raise ValueError("gu must be [n_rows][2*inter]")
     k = gu.shape[1] // 2
     return silu(gu[:, :k]) * gu[:, k:]
+
+
+def _bf16_rne_bits(x):
+    """f32 -> bf16 bit pattern, round to nearest even (f32_to_bf16_rne on the memra-engine
+    qwen4exp_gpu.rs page); finite inputs."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def quantize(wf):
+    """Affine-Q4 quantiser for dense f32 rows [n][in] (in % 64 == 0), following the steps of
+    the affine 5-bit host codec host_quant_q5_row (memra-engine qwen4exp_gpu.rs page) with
+    16 levels and 64-wide groups, in f32: mn, mx = min, max of the group; d = (mx - mn) / 15;
+    id = 1 / d (0 when d == 0 or 1/d is not finite); q = clamp(rint((w - mn) * id), 0, 15).
+    Returns codes u8 [n][in], scales and biases as bf16 bits [n][in/64] (bf16(d), bf16(mn)),
+    and the f32 d and mn."""
+    wf = np.ascontiguousarray(wf, dtype=np.float32)
+    if wf.ndim != 2 or wf.shape[1] % GROUP:
+        raise ValueError("wf must be [n_rows][in_dim] with in_dim % 64 == 0")
+    n, k = wf.shape
+    g = wf.reshape(n, k // GROUP, GROUP)
+    mn = g.min(axis=2)
+    mx = g.max(axis=2)
+    d = ((mx - mn) / np.float32(15.0)).astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        inv = np.where(d != 0, np.float32(1.0) / d, np.float32(0.0)).astype(np.float32)
+    inv[~np.isfinite(inv)] = 0.0
+    t = np.rint((g - mn[:, :, None]) * inv[:, :, None]).astype(np.float32)
+    q = np.clip(t, 0, 15).astype(np.uint8).reshape(n, k)
+    return q, _bf16_rne_bits(d), _bf16_rne_bits(mn), d, mn

@@ -141,3 +141,14 @@ def test_swiglu_prep_validation(L):
     assert f(A + 4, 1, 640, A, A, A, None) == EALIGN
     assert f(A, 1, 640, A + 8, A, A, None) == EALIGN
     assert f(A, 1, 640, A, A, A + 2, None) == EALIGN
+
+
+def test_quantize_validation(L):
+    f = L.q4mv_quantize
+    assert f(None, A, A, A, 1, 64, None) == ENULL
+    assert f(A, A, None, A, 1, 64, None) == ENULL
+    assert f(A, A, A, A, 0, 64, None) == ESHAPE
+    assert f(A, A, A, A, 1, 96, None) == ESHAPE
+    assert f(A + 4, A, A, A, 1, 64, None) == EALIGN
+    assert f(A, A + 2, A, A, 1, 64, None) == EALIGN
+    assert f(A, A, A + 1, A, 1, 64, None) == EALIGN

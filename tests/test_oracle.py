@@ -376,3 +376,56 @@ def test_swiglu_closed_forms(oracle_lib):
     big = oracle.swiglu(np.concatenate([np.full((1, 64), 50.0), u[:1]], axis=1))
     np.testing.assert_allclose(big, 50.0 * u[:1], rtol=1e-15)
     assert np.all(oracle.swiglu(np.concatenate([np.zeros((1, 64)), u[:1]], axis=1)) == 0)
+
+
+# --- affine-Q4 quantiser (steps of host_quant_q5_row, memra-engine qwen4exp_gpu.rs page) ----
+
+def test_quantize_reconstruction_bound(oracle_lib):
+    # every weight is within d/2 of d*q + mn (the rounding step), up to f32 slack, and the
+    # group's minimum gets code 0 and its maximum code 15
+    rng = np.random.default_rng(3)
+    wf = (rng.normal(0, 0.02, (6, 512)) + rng.normal(0, 0.1, (6, 1))).astype(np.float32)
+    q, s_bits, b_bits, d, mn = oracle_lib.quantize(wf)
+    g = wf.reshape(6, 8, 64).astype(np.float64)
+    rec = d[:, :, None].astype(np.float64) * q.reshape(6, 8, 64) + mn[:, :, None]
+    slack = 4 * 2.0 ** -24 * (np.abs(g).max(axis=2) + 15 * d)[:, :, None]
+    assert np.all(np.abs(rec - g) <= d[:, :, None] / 2 + slack)
+    qq = q.reshape(6, 8, 64)
+    assert np.all(qq[np.arange(6)[:, None], np.arange(8)[None, :], g.argmin(axis=2)] == 0)
+    assert np.all(qq[np.arange(6)[:, None], np.arange(8)[None, :], g.argmax(axis=2)] == 15)
+    # the stored bf16 values decode to within half a bf16 ulp (2^-8 relative) of d and mn
+    sd = workloads.bf16_bits_to_f32(s_bits).astype(np.float64)
+    bd = workloads.bf16_bits_to_f32(b_bits).astype(np.float64)
+    assert np.all(np.abs(sd - d) <= 2.0 ** -8 * np.abs(d))
+    assert np.all(np.abs(bd - mn) <= 2.0 ** -8 * np.abs(mn))
+
+
+def test_quantize_closed_forms(oracle_lib):
+    # a group on an exact grid mn + k*2^-6 (k = 0..15) gets codes k; a constant group gets
+    # d = 0, codes 0 and bias = the constant
+    k = np.arange(64) % 16
+    wf = np.stack([-0.25 + k * 2.0 ** -6, np.full(64, 0.75)]).astype(np.float32)
+    q, s_bits, b_bits, d, mn = oracle_lib.quantize(wf)
+    np.testing.assert_array_equal(q[0], k)
+    assert d[0, 0] == np.float32(2.0 ** -6) and mn[0, 0] == np.float32(-0.25)
+    np.testing.assert_array_equal(q[1], 0)
+    assert d[1, 0] == 0 and s_bits[1, 0] == 0
+    assert workloads.bf16_bits_to_f32(b_bits[1:2, :1])[0, 0] == np.float32(0.75)
+
+
+def test_quantize_then_gemv(oracle_lib):
+    # the quantised matrix times x stays within sum_i |x_i| * (d/2 + bf16 rounding of the
+    # scale (times up to 15) and the bias) of the
+    # dense product, computed by the GEMV oracle on the stored codes, scales and biases
+    rng = np.random.default_rng(8)
+    wf = rng.normal(0, 0.02, (96, 256)).astype(np.float32)
+    x = rng.normal(0, 1, (1, 2, 256)).astype(np.float32)
+    q, s_bits, b_bits, d, mn = oracle_lib.quantize(wf)
+    y, _ = oracle_lib.gemv(q.reshape(1, 96, 256), s_bits.reshape(1, 96, 4),
+                           b_bits.reshape(1, 96, 4), x)
+    dense = (x[0].astype(np.float64) @ wf.T.astype(np.float64))
+    dmax = np.repeat(d, 64, axis=1).astype(np.float64)
+    mabs = np.repeat(np.abs(mn), 64, axis=1).astype(np.float64)
+    per_w = dmax / 2 + 2.0 ** -8 * (15 * dmax + mabs) + 1e-7
+    lim = np.abs(x[0]).astype(np.float64) @ per_w.T
+    assert np.all(np.abs(y[0] - dense) <= lim)
