@@ -16,6 +16,8 @@ never imports it.
 * :func:`silu`, :func:`gemv_silu`, :func:`swiglu` -- the fused epilogues of the same page:
   ``fn_qmv_silu_b`` stores silu(y / div), and ``fn_moe_act_b`` forms silu(gate) * up from the
   stacked gate/up output before the down projection's prep.
+* :func:`experts`, :func:`combine` -- the selected-expert dispatch (a bank, expert ids,
+  shared or per-expert activation rows) and the routing-weighted sum of the expert outputs.
 """
 from __future__ import annotations
 
@@ -176,6 +178,48 @@ def swiglu(gu):
         raise ValueError("gu must be [n_rows][2*inter]")
     k = gu.shape[1] // 2
     return silu(gu[:, :k]) * gu[:, k:]
+
+
+def experts(codes, scales, biases, sel, x, x_shared, nthreads: int | None = None):
+    """Selected-expert GEMV (launch_qmatvec_bf16w_sel on the memra-engine qwen4exp_gpu.rs page:
+    a bank of matrices, a list of expert ids and an activation stride that may be zero; the
+    unique-expert loop of fn_moe_gate_up_b / fn_moe_down_b on the Constant BATCH_MSL page).
+    Slot u applies bank matrix sel[u] to activation rows x [nb][in] when x_shared, else to
+    x[u] of x [n_sel][nb][in]. Returns y and the per-element bound, f64 [n_sel][nb][out]; a
+    slot whose id is outside the bank is NaN (bound 0)."""
+    codes = np.asarray(codes)
+    sel = np.asarray(sel, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float32)
+    if sel.ndim != 1 or sel.size == 0:
+        raise ValueError("sel must be a non-empty 1-D id list")
+    ok = (sel >= 0) & (sel < codes.shape[0])
+    e = np.where(ok, sel, 0)
+    if x_shared:
+        if x.ndim != 2:
+            raise ValueError("shared activations: x [nb][in] expected")
+        xs = np.broadcast_to(x[None], (sel.size,) + x.shape)
+    else:
+        if x.ndim != 3 or x.shape[0] != sel.size:
+            raise ValueError("per-slot activations: x [n_sel][nb][in] expected")
+        xs = x
+    y, bound = gemv(codes[e], np.asarray(scales)[e], np.asarray(biases)[e], xs,
+                    nthreads=nthreads)
+    y[~ok] = np.nan
+    bound[~ok] = 0.0
+    return y, bound
+
+
+def combine(y, wmap):
+    """Routing-weighted expert sum (the expert sum of fn_moe_combine_b on the Constant
+    BATCH_MSL page): out[r][o] = sum_u wmap[r][u] * y[u][r][o] in f64, for y [n_u][nb][out]
+    and wmap [nb][n_u]. Also returns sum_u |wmap[r][u] * y[u][r][o]|, the scale of the
+    rounding error of any order of f32 multiply-adds."""
+    y = np.asarray(y, dtype=np.float64)
+    wmap = np.asarray(wmap, dtype=np.float64)
+    if y.ndim != 3 or wmap.shape != (y.shape[1], y.shape[0]):
+        raise ValueError("y [n_u][nb][out] and wmap [nb][n_u] expected")
+    terms = wmap.T[:, :, None] * y
+    return terms.sum(axis=0), np.abs(terms).sum(axis=0)
 
 
 def _bf16_rne_bits(x):

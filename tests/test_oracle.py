@@ -429,3 +429,73 @@ def test_quantize_then_gemv(oracle_lib):
     per_w = dmax / 2 + 2.0 ** -8 * (15 * dmax + mabs) + 1e-7
     lim = np.abs(x[0]).astype(np.float64) @ per_w.T
     assert np.all(np.abs(y[0] - dense) <= lim)
+
+
+def _probe_bank(n_bank, out_dim, in_dim):
+    """All codes 0, so y = sum_g bias * sum_x; bank matrix e, row o has bias (e+1) + 8*o in
+    every group (small integers, exact in bf16): the output names the matrix and the row."""
+    codes = np.zeros((n_bank, out_dim, in_dim), dtype=np.uint8)
+    vals = (np.arange(n_bank)[:, None] + 1 + 8 * np.arange(out_dim)[None, :]).astype(np.float32)
+    biases = np.repeat(workloads.f32_to_bf16_bits(vals)[:, :, None], in_dim // 64, axis=2)
+    rng = np.random.default_rng(3)
+    scales = workloads.f32_to_bf16_bits(rng.normal(0, 1, biases.shape).astype(np.float32))
+    return codes, scales, biases, vals
+
+
+def test_experts_pick_matrix_and_rows(oracle_lib):
+    n_bank, out_dim, in_dim, nb = 5, 4, 128, 3
+    codes, scales, biases, vals = _probe_bank(n_bank, out_dim, in_dim)
+    sel = np.array([3, 0, 3, 4], dtype=np.int32)  # repeats and any order
+    # per-slot rows: slot u row r is the constant (u*nb + r + 1) / 64 (exact)
+    c = (np.arange(sel.size * nb) + 1).reshape(sel.size, nb) / 64.0
+    x = np.repeat(c[:, :, None], in_dim, axis=2).astype(np.float32)
+    y, bound = oracle_lib.experts(codes, scales, biases, sel, x, x_shared=False)
+    want = in_dim * c[:, :, None] * vals[sel][:, None, :]
+    assert np.array_equal(y, want)
+    assert np.array_equal(bound, np.abs(want))
+    # shared rows: every slot reads rows 0..nb-1 (row r = (r + 1) / 64)
+    y, _ = oracle_lib.experts(codes, scales, biases, sel, x[0], x_shared=True)
+    assert np.array_equal(y, in_dim * c[0][None, :, None] * vals[sel][:, None, :])
+
+
+def test_experts_bad_ids_are_nan(oracle_lib):
+    codes, scales, biases, vals = _probe_bank(3, 2, 64)
+    x = np.ones((2, 64), dtype=np.float32)
+    y, bound = oracle_lib.experts(codes, scales, biases, [2, -1, 3, 1], x, x_shared=True)
+    assert np.all(np.isnan(y[[1, 2]])) and np.all(bound[[1, 2]] == 0)
+    assert np.array_equal(y[0], np.broadcast_to(64 * vals[2], (2, 2)))
+    assert np.array_equal(y[3], np.broadcast_to(64 * vals[1], (2, 2)))
+
+
+def test_experts_equal_stacked_gemv(oracle_lib):
+    """Slot u over bank matrix sel[u] equals the dense double matvec of that matrix (a
+    reference with its own bf16 decoder)."""
+    case = workloads.make_shape(6, 48, 192, 2, seed=31)
+    sel = np.array([5, 1, 1, 0], dtype=np.int32)
+    x = workloads.make_x(sel.size, 2, 192, seed=32)
+    y, _ = oracle_lib.experts(case["codes"], case["scales"], case["biases"], sel, x, False)
+    ref, _ = dense_reference(case["codes"][sel], case["scales"][sel], case["biases"][sel], x)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_combine_closed_forms(oracle_lib):
+    rng = np.random.default_rng(5)
+    n_u, nb, out_dim = 4, 3, 5
+    y = rng.normal(size=(n_u, nb, out_dim))
+    # one-hot weights select a slot per token
+    pick = np.array([2, 0, 3])
+    onehot = np.zeros((nb, n_u))
+    onehot[np.arange(nb), pick] = 1.0
+    out, _ = oracle_lib.combine(y, onehot)
+    assert np.array_equal(out, y[pick, np.arange(nb)])
+    # all-ones weights sum the slots; zero weights give zero
+    out, mag = oracle_lib.combine(y, np.ones((nb, n_u)))
+    assert np.allclose(out, y.sum(axis=0), rtol=1e-15, atol=1e-15)
+    assert np.allclose(mag, np.abs(y).sum(axis=0), rtol=1e-15)
+    out, mag = oracle_lib.combine(y, np.zeros((nb, n_u)))
+    assert not out.any() and not mag.any()
+    # hand-worked: token 0 = 2*y[0] - y[1], token 1 = y[1]/2 (integers, exact)
+    y = np.arange(2 * 2 * 3, dtype=np.float64).reshape(2, 2, 3)
+    out, mag = oracle_lib.combine(y, [[2.0, -1.0], [0.0, 0.5]])
+    assert np.array_equal(out, [[-6.0, -5.0, -4.0], [4.5, 5.0, 5.5]])
+    assert np.array_equal(mag, [[6.0, 9.0, 12.0], [4.5, 5.0, 5.5]])

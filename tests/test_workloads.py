@@ -54,3 +54,17 @@ def test_weight_bytes():
     assert workloads.weight_bytes(1, 9728, 2560) == 14008320
     assert workloads.weight_bytes(1, 151936, 2560) == 218787840
     assert workloads.weight_bytes(8, 2560, 640) == 7372800
+
+
+def test_routing_recipe():
+    for seed in range(4):
+        sel, wmap = workloads.make_routing(4, 32, 8, seed=seed)
+        assert sel.dtype == np.int32 and np.all(np.diff(sel) > 0)
+        assert sel.min() >= 0 and sel.max() < 32
+        assert wmap.shape == (4, sel.size) and wmap.dtype == np.float32
+        assert np.all((wmap > 0).sum(axis=1) == 8)
+        assert np.all((wmap > 0).any(axis=0))  # every slot is some token's pick
+        assert np.allclose(wmap.sum(axis=1), 1.0, atol=1e-6)
+    a = workloads.make_routing(4, 32, 8, seed=1)
+    b = workloads.make_routing(4, 32, 8, seed=1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -112,6 +112,21 @@ def make_shape(n_mat: int, out_dim: int, in_dim: int, nb: int, seed: int = 0,
                 x_scale=x_scale)
 
 
+def make_routing(nb: int, n_experts: int, top_k: int, seed: int = 0):
+    """Synthetic top-k routing of nb tokens over n_experts: each token picks top_k distinct
+    experts uniformly at random, with weights drawn uniform on [0.05, 1) and divided by their
+    sum in f32. Returns the union of the picked experts (``sel``, sorted ascending, i32) and
+    ``wmap`` f32 [nb][len(sel)], token r's weight for slot u (0 where r did not pick it)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    picks = [rng.choice(n_experts, size=top_k, replace=False) for _ in range(nb)]
+    sel = np.unique(np.concatenate(picks)).astype(np.int32)
+    wmap = np.zeros((nb, sel.size), dtype=np.float32)
+    for r, p in enumerate(picks):
+        w = rng.uniform(0.05, 1.0, size=top_k).astype(np.float32)
+        wmap[r, np.searchsorted(sel, p)] = w / w.sum(dtype=np.float32)
+    return sel, wmap
+
+
 def weight_bytes(n_mat: int, out_dim: int, in_dim: int) -> int:
     """Bytes of packed codes (0.5 B per weight) plus bf16 scale and bias per 64-group."""
     return n_mat * out_dim * (in_dim // 2 + 4 * (in_dim // GROUP))
