@@ -57,6 +57,8 @@ def lib():
         L.q4mv_path_silu.argtypes = gemv + [f32, i32, p]
         L.q4mv_swiglu_prep.argtypes = [p, i32, i32, p, p, p, p]
         L.q4mv_quantize.argtypes = [p, p, p, p, i64, i32, p]
+        L.q4mv_experts.argtypes = [p, p, p, i32, p, i32, p, p, p, p] + [i32] * 5 + [p]
+        L.q4mv_combine.argtypes = [p, p, p, i32, i32, i32, p]
         L.q4mv_auto_path.argtypes = [i32, i32, i32, i32]
         L.q4mv_status_str.argtypes = [i32]
         L.q4mv_status_str.restype = ctypes.c_char_p
@@ -229,6 +231,52 @@ def q4mv_swiglu_prep(gu, xe=None, xo=None, xsum=None, stream=None):
                                                        xo.data_ptr(), xsum.data_ptr(),
                                                        _stream(gu, stream)))
     return xe, xo, xsum
+
+
+def q4mv_experts(w, scales, biases, sel, xe, xo, xsum, nb, x_shared, path=PATH_AUTO, y=None,
+                 stream=None):
+    """Slot u = bank matrix sel[u] (int32 GPU tensor) over its activation rows: rows 0..nb-1
+    for every slot when x_shared, else rows u*nb .. u*nb+nb-1 -> y f32 [n_sel, nb, out_dim]."""
+    torch = _torch()
+    if w.dim() != 3:
+        raise ValueError("w: expected [n_bank, out_dim, in_dim/8]")
+    n_bank, out_dim, w8 = w.shape
+    in_dim = w8 * 8
+    _need(w, torch.int32, (n_bank, out_dim, w8), "w")
+    _need(scales, torch.bfloat16, (n_bank, out_dim, in_dim // 64), "scales")
+    _need(biases, torch.bfloat16, (n_bank, out_dim, in_dim // 64), "biases")
+    if sel.dim() != 1:
+        raise ValueError("sel: expected [n_sel]")
+    n_sel = sel.shape[0]
+    _need(sel, torch.int32, (n_sel,), "sel")
+    rows = nb if x_shared else n_sel * nb
+    _need(xe, torch.float16, (rows, in_dim // 2), "xe")
+    _need(xo, torch.float16, (rows, in_dim // 2), "xo")
+    _need(xsum, torch.float32, (rows, in_dim // 32), "xsum")
+    if y is None:
+        y = torch.empty((n_sel, nb, out_dim), dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, (n_sel, nb, out_dim), "y")
+    _check("q4mv_experts", lib().q4mv_experts(
+        w.data_ptr(), scales.data_ptr(), biases.data_ptr(), n_bank, sel.data_ptr(), n_sel,
+        xe.data_ptr(), xo.data_ptr(), xsum.data_ptr(), y.data_ptr(), out_dim, in_dim, nb,
+        int(bool(x_shared)), int(path), _stream(w, stream)))
+    return y
+
+
+def q4mv_combine(y, wmap, out=None, stream=None):
+    """y f32 [n_u, nb, out_dim], wmap f32 [nb, n_u] -> out f32 [nb, out_dim]."""
+    torch = _torch()
+    if y.dim() != 3:
+        raise ValueError("y: expected [n_u, nb, out_dim]")
+    n_u, nb, out_dim = y.shape
+    _need(y, torch.float32, (n_u, nb, out_dim), "y")
+    _need(wmap, torch.float32, (nb, n_u), "wmap")
+    if out is None:
+        out = torch.empty((nb, out_dim), dtype=torch.float32, device=y.device)
+    _need(out, torch.float32, (nb, out_dim), "out")
+    _check("q4mv_combine", lib().q4mv_combine(y.data_ptr(), wmap.data_ptr(), out.data_ptr(),
+                                               n_u, nb, out_dim, _stream(y, stream)))
+    return out
 
 
 def q4mv_auto_path(in_dim: int, nb: int, two_row: bool = False, out_dim: int = 2) -> int:

@@ -177,6 +177,42 @@ int q4mv_path_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *bi
                     div);
 }
 
+int q4mv_experts(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, int n_bank,
+                 const int32_t *sel, int n_sel, const void *xe, const void *xo,
+                 const float *xsum, float *y, int out_dim, int in_dim, int nb, int x_shared,
+                 int path, void *stream)
+{
+    if (!w || !scales || !biases || !sel || !xe || !xo || !xsum || !y) return Q4MV_ERR_NULL;
+    if (n_bank < 1 || n_sel < 1 || n_sel > 65535 || out_dim < 1 || in_dim < 64 ||
+        in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB ||
+        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(sel, 4) ||
+        !aligned(xe, 16) || !aligned(xo, 16) || !aligned(xsum, 4) || !aligned(y, 4))
+        return Q4MV_ERR_ALIGN;
+    if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
+    if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
+    if (path < 0) return path;
+    if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
+    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_sel * ((out_dim + 31) / 32)).wpb == 0)
+        return Q4MV_ERR_SHAPE;
+    GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_sel, out_dim, in_dim, nb, 0.0f,
+               static_cast<hipStream_t>(stream), sel, n_bank, x_shared != 0};
+    hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
+int q4mv_combine(const float *y, const float *wmap, float *out, int n_u, int nb, int out_dim,
+                 void *stream)
+{
+    if (!y || !wmap || !out) return Q4MV_ERR_NULL;
+    if (n_u < 1 || nb < 1 || out_dim < 1 || (long long)nb * out_dim > (1LL << 31))
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(y, 4) || !aligned(wmap, 4) || !aligned(out, 4)) return Q4MV_ERR_ALIGN;
+    hipError_t e = launch_combine(y, wmap, out, n_u, nb, out_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
 int q4mv_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint16_t *biases,
                   int64_t n_rows, int in_dim, void *stream)
 {
@@ -245,6 +281,6 @@ const char *q4mv_status_str(int status)
     }
 }
 
-int q4mv_version(void) { return 200; }
+int q4mv_version(void) { return 300; }
 
 }  // extern "C"

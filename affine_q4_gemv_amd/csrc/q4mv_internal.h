@@ -17,6 +17,12 @@ struct GemvArgs {
     int n_mat, out_dim, in_dim, nb;
     float epi_div;  // 0: y = the product; else y = silu(product / epi_div)
     hipStream_t stream;
+    // Selected experts (sel null: matrix m is the m-th of the n_mat contiguous at w, scales,
+    // biases): slot m uses bank matrix sel[m] of n_bank. x_shared: every slot reads
+    // activation rows 0..nb-1 (else slot m reads rows m*nb .. m*nb+nb-1).
+    const int *sel = nullptr;
+    int n_bank = 0;
+    int x_shared = 0;
 };
 
 // Kernel paths (same numbering as q4mv_path in q4mv.h).
@@ -35,6 +41,8 @@ inline int valu_log2g(int in_dim)
 int auto_path(int in_dim, int nb, bool two_row, int out_dim);
 
 hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s);
+hipError_t launch_combine(const float *y, const float *wmap, float *out, int n_u, int nb,
+                          int out_dim, hipStream_t s);
 hipError_t launch_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint16_t *biases,
                            int64_t n_rows, int in_dim, hipStream_t s);
 hipError_t launch_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo,

@@ -75,7 +75,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
-    int out_dim, int in_dim, int nb, float epi_div)
+    int out_dim, int in_dim, int nb, float epi_div, const int *__restrict__ sel,
+    int n_bank, int x_shared)
 {
     constexpr int TH = WPB * 64;
     constexpr int TPB = WPB / KS;  // tile groups per block
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // Stage activations and group sums. Called after each wave has issued its first weight
     // loads, so the two latencies overlap.
     auto stage = [&]() {
-        const size_t xrow0 = (size_t)m * nb;
+        const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
         const uint2 *xe_m = xe + xrow0 * words8;
         const uint2 *xo_m = xo + xrow0 * words8;
         const float *xsum_m = xsum + xrow0 * C;
@@ -166,9 +167,18 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // out_dim (its overlap with the previous tile is recomputed with identical arithmetic
     // and stored again with the same bits). Only when out_dim < 32 are rows clamped.
     const bool narrow = out_dim < 32;
-    const uint4 *const w_m = w + (size_t)m * out_dim * C;
-    const uint16_t *const s_m = scales + (size_t)m * out_dim * groups;
-    const uint16_t *const b_m = biases + (size_t)m * out_dim * groups;
+    // Weights: matrix m, or bank matrix sel[m]. An id outside the bank reads matrix 0 and
+    // stores NaN (a NaN divisor makes the epilogue return NaN).
+    int e = m;
+    if (sel) {
+        const int id = sel[m];
+        const bool bad = (unsigned)id >= (unsigned)n_bank;
+        e = bad ? 0 : id;
+        if (bad) epi_div = __builtin_nanf("");
+    }
+    const uint4 *const w_m = w + (size_t)e * out_dim * C;
+    const uint16_t *const s_m = scales + (size_t)e * out_dim * groups;
+    const uint16_t *const b_m = biases + (size_t)e * out_dim * groups;
     float *const y_m = y + (size_t)m * nb * out_dim;
     auto tile_row = [&](int tile) { return narrow ? 0 : min(tile * 32, out_dim - 32); };
 
@@ -357,7 +367,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 }
 
 typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
-                       const uint2 *, const float *, float *, int, int, int, float);
+                       const uint2 *, const float *, float *, int, int, int, float,
+                       const int *, int, int);
 
 template <int WPB, int KS>
 static MfmaFn pick(bool nb16, bool sb8)
@@ -396,6 +407,7 @@ hipError_t launch_mfma(const GemvArgs &a)
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
     const size_t lds = mfma_lds_bytes(a.in_dim, a.nb) + mfma_part_bytes(sh.wpb, sh.ks, nb16) +
                        (size_t)sh.wpb * kScratchUnits * 16;
+    // (with an expert table the scale addresses are not known on the host: 2-byte loads)
     const bool sb8 = groups % 4 == 0 && (uintptr_t)a.scales % 8 == 0 &&
                      (uintptr_t)a.biases % 8 == 0;
     MfmaFn fn;
@@ -425,7 +437,7 @@ hipError_t launch_mfma(const GemvArgs &a)
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(sh.wpb * 64), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
-                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, a.epi_div);
+                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, a.epi_div, a.sel, a.n_bank, a.x_shared);
     return hipGetLastError();
 }
 

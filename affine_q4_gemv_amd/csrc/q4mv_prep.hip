@@ -153,6 +153,32 @@ hipError_t launch_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint1
     return hipGetLastError();
 }
 
+// Routing-weighted combine of expert outputs (the combine of the grouped-expert dispatch on
+// the Constant BATCH_MSL page): out[r][o] = sum over u of wmap[r][u] * y[u][r][o], u taken in
+// order 0..n_u-1 with one fused multiply-add each. One thread per (r, o).
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
+                                                      const float *__restrict__ wmap,
+                                                      float *__restrict__ out, int n_u, int nb,
+                                                      int out_dim)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)nb * out_dim) return;
+    const int r = (int)(i / out_dim);
+    const int64_t stride = (int64_t)nb * out_dim;
+    float acc = 0.0f;
+    for (int u = 0; u < n_u; u++) acc = __builtin_fmaf(wmap[(int64_t)r * n_u + u], y[u * stride + i], acc);
+    out[i] = acc;
+}
+
+hipError_t launch_combine(const float *y, const float *wmap, float *out, int n_u, int nb,
+                          int out_dim, hipStream_t s)
+{
+    const int64_t n = (int64_t)nb * out_dim;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y,
+                       wmap, out, n_u, nb, out_dim);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s)
 {
     const int64_t n_words = n_codes / 8;

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
-    int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt, float epi_div)
+    int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt, float epi_div,
+    const int *__restrict__ sel, int n_bank, int x_shared)
 {
     const int log2g = LOG2G >= 0 ? LOG2G : log2g_rt;
     extern __shared__ uint4 lds[];
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     // Stage activation rows r0 .. r0+NB-1 of matrix m (pair layout + scaled sums) in LDS.
     // stage_load issues one round of loads into registers and stage_store writes them, so a
     // wave can put its first weight loads between the two and the latencies overlap.
-    const size_t xrow0 = (size_t)m * nb_total + r0;
+    const size_t xrow0 = (x_shared ? 0 : (size_t)m * nb_total) + r0;
     const uint2 *xe_m = xe + xrow0 * words8;
     const uint2 *xo_m = xo + xrow0 * words8;
     const float *xsum_m = xsum + xrow0 * C;
@@ -142,9 +143,18 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     const int wstride = gridDim.x * (kValuThreads / 64);
     const int cpl = CPL > 0 ? CPL : cpl_rt;
 
-    const uint4 *w_m = w + (size_t)m * out_dim * C;
-    const uint16_t *s_m = scales + (size_t)m * out_dim * groups;
-    const uint16_t *b_m = biases + (size_t)m * out_dim * groups;
+    // Weights: matrix m, or bank matrix sel[m]. An id outside the bank reads matrix 0 and
+    // stores NaN (a NaN divisor makes the epilogue return NaN).
+    int e = m;
+    if (sel) {
+        const int id = sel[m];
+        const bool bad = (unsigned)id >= (unsigned)n_bank;
+        e = bad ? 0 : id;
+        if (bad) epi_div = __builtin_nanf("");
+    }
+    const uint4 *w_m = w + (size_t)e * out_dim * C;
+    const uint16_t *s_m = scales + (size_t)e * out_dim * groups;
+    const uint16_t *b_m = biases + (size_t)e * out_dim * groups;
     float *y_m = y + ((size_t)m * nb_total + r0) * out_dim;
 
     // activations in registers for the whole kernel when they fit
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     // lane's chunks of every activation row, converted to the pair layout.
     auto load_xreg_direct = [&]() {
         if constexpr (XREG) {
-            const size_t xrow0 = (size_t)m * nb_total + r0;
+            const size_t xrow0 = (x_shared ? 0 : (size_t)m * nb_total) + r0;
 #pragma unroll
             for (int k = 0; k < CPL; k++) {
                 const int c = j + (k << log2g);
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
 
 typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, int, int, int,
-                       float);
+                       float, const int *, int, int);
 
 // (log2 G, CPL) of the specialised row lengths: in_dim = 32 * CPL << log2G.
 #define Q4MV_VALU_SHAPES(X)                                                                   \
@@ -511,7 +521,8 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(kValuThreads), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
-                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, r0, log2g, cpl, a.epi_div);
+                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, r0, log2g, cpl, a.epi_div,
+                       a.sel, a.n_bank, a.x_shared);
     return hipGetLastError();
 }
 

@@ -259,6 +259,67 @@ class MoeChain(Problem):
             raise RuntimeError("graph replay output differs from the eager call")
 
 
+class MoeLayer(MoeChain):
+    """A decode MoE layer over routed experts: a bank of 32 experts (hidden 2560, intermediate
+    640), 4 tokens with synthetic top-8 routing. One step = activation prep + gate|up over the
+    routed experts (shared token rows) + SwiGLU prep + down per expert + combine (five
+    launches); the weights read are those of the routed experts only."""
+
+    def __init__(self, n_exp=32, hidden=2560, inter=640, nb=4, top_k=8):
+        import numpy as np
+        import torch
+
+        import affine_q4_gemv_amd as q4
+        import workloads
+        self.q4, self.torch = q4, torch
+        self.silu_div = None
+        dev = torch.device("cuda:0")
+        sel, wmap = workloads.make_routing(nb, n_exp, top_k, seed=71)
+        self.n_u = n_u = sel.size
+        gu = workloads.make_shape(n_exp, 2 * inter, hidden, nb, seed=72)
+        dn = workloads.make_weights(n_exp, hidden, inter, seed=73)
+
+        def put(codes, scales, biases):
+            w = q4.q4mv_pack_codes(torch.from_numpy(codes).to(dev))
+            s = torch.from_numpy(scales.view(np.int16)).to(dev).view(torch.bfloat16)
+            b = torch.from_numpy(biases.view(np.int16)).to(dev).view(torch.bfloat16)
+            return w, s, b
+        bank_bytes = (workloads.weight_bytes(n_exp, 2 * inter, hidden)
+                      + workloads.weight_bytes(n_exp, hidden, inter))
+        self.weight_bytes = (workloads.weight_bytes(n_u, 2 * inter, hidden)
+                             + workloads.weight_bytes(n_u, hidden, inter))
+        self.R = max(1, math.ceil(ROTATE_BYTES / bank_bytes))
+        w1, s1, b1 = put(gu["codes"], gu["scales"], gu["biases"])
+        w2, s2, b2 = put(*dn)
+        self.sets = [(w1, s1, b1, w2, s2, b2)] + [
+            tuple(t.clone() for t in (w1, s1, b1, w2, s2, b2)) for _ in range(self.R - 1)]
+        self.sel = torch.from_numpy(sel).to(dev)
+        self.wmap = torch.from_numpy(wmap).to(dev)
+        self.x = torch.from_numpy(np.ascontiguousarray(gu["x"][0])).to(dev)
+        self.xe = torch.empty((nb, hidden // 2), dtype=torch.float16, device=dev)
+        self.xo = torch.empty_like(self.xe)
+        self.xsum = torch.empty((nb, hidden // 32), dtype=torch.float32, device=dev)
+        self.gu = torch.empty((n_u, nb, 2 * inter), dtype=torch.float32, device=dev)
+        self.xe2 = torch.empty((n_u * nb, inter // 2), dtype=torch.float16, device=dev)
+        self.xo2 = torch.empty_like(self.xe2)
+        self.xsum2 = torch.empty((n_u * nb, inter // 32), dtype=torch.float32, device=dev)
+        self.yd = torch.empty((n_u, nb, hidden), dtype=torch.float32, device=dev)
+        self.y = torch.empty((nb, hidden), dtype=torch.float32, device=dev)
+        self.nb, self.inter = nb, inter
+        torch.cuda.synchronize()
+
+    def gemv(self, i):
+        w1, s1, b1, w2, s2, b2 = self.sets[i % self.R]
+        q4, nb = self.q4, self.nb
+        q4.q4mv_prepare_x(self.x, self.xe, self.xo, self.xsum)
+        q4.q4mv_experts(w1, s1, b1, self.sel, self.xe, self.xo, self.xsum, nb, True, y=self.gu)
+        q4.q4mv_swiglu_prep(self.gu.view(self.n_u * nb, 2 * self.inter), self.xe2, self.xo2,
+                            self.xsum2)
+        q4.q4mv_experts(w2, s2, b2, self.sel, self.xe2, self.xo2, self.xsum2, nb, False,
+                        y=self.yd)
+        q4.q4mv_combine(self.yd, self.wmap, out=self.y)
+
+
 def cpu_baseline(name, nb, budget_s=10.0):
     """The CPU oracle on the full workload, repeated for about budget_s seconds (at least
     three passes); the median pass time gives the rate."""
@@ -510,6 +571,17 @@ def main():
         gbps = p.weight_bytes / (ms * 1e-3) / 1e9
         sweep.append({"workload": "moe_mlp 8x(2560->2x640->2560)", "nb": 4,
                       "launches": "gate|up GEMV + SwiGLU prep + down GEMV",
+                      "step_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
+                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
+        del p
+        torch.cuda.empty_cache()
+        p = MoeLayer()
+        ms = p.time_kernel(200)
+        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+        sweep.append({"workload": f"moe_layer top-8 of 32 experts (2560->2x640->2560), "
+                                  f"{p.n_u} routed", "nb": 4,
+                      "launches": "prep + gate|up experts + SwiGLU prep + down experts + "
+                                  "combine",
                       "step_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
                       "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
         del p

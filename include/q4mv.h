@@ -177,6 +177,44 @@ int q4mv_path_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *bi
 int q4mv_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo, float *xsum,
                      void *stream);
 
+/*
+ * q4mv_experts -- the GEMV over selected matrices of a bank (the selected-expert launch
+ * launch_qmatvec_bf16w_sel on the qwen4exp_gpu.rs page: a bank, a device array of expert
+ * ids and an activation stride that may be 0; and the unique-expert dispatch of
+ * fn_moe_gate_up_b / fn_moe_down_b on the Constant BATCH_MSL page):
+ *   w, scales, biases : the bank, n_bank matrices in the q4mv layout
+ *   sel     : i32 [n_sel] device array; slot u computes with bank matrix sel[u]
+ *   xe, xo, xsum : q4mv_prepare_x output with n_rows = nb (x_shared != 0: every slot reads
+ *             activation rows 0..nb-1, e.g. the gate/up projection of one token batch) or
+ *             n_rows = n_sel*nb (x_shared == 0: slot u reads rows u*nb .. u*nb+nb-1, e.g.
+ *             the down projection of each expert's own SwiGLU output)
+ *   y       : f32 [n_sel][nb][out_dim]   fully overwritten
+ *   path    : as q4mv_path (0 = automatic dispatch on (in_dim, nb, out_dim))
+ * Slot u's result is bitwise what q4mv gives for bank matrix sel[u] and the same
+ * activation rows. The ids live on the device and are not read by the host: a slot whose
+ * id is outside 0..n_bank-1 reads no memory outside the bank and its y rows are NaN.
+ * Errors: NULL pointer; n_bank < 1, n_sel outside 1..65535, and the shape errors of q4mv
+ * (SHAPE); sel not 4-byte aligned or the alignment errors of q4mv (ALIGN); PATH, ODD_ROWS,
+ * and SHAPE for path 3 as q4mv_path; launch failure.
+ */
+int q4mv_experts(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                 int n_bank, const int32_t *sel, int n_sel, const void *xe, const void *xo,
+                 const float *xsum, float *y, int out_dim, int in_dim, int nb, int x_shared,
+                 int path, void *stream);
+
+/*
+ * q4mv_combine -- routing-weighted sum of expert outputs (the expert sum of
+ * fn_moe_combine_b on the Constant BATCH_MSL page, without its shared-expert gate):
+ *   y    : f32 [n_u][nb][out_dim]   e.g. q4mv_experts output
+ *   wmap : f32 [nb][n_u]            token r's weight for slot u (0 where r did not route to u)
+ *   out  : f32 [nb][out_dim]        out[r][o] = sum over u = 0..n_u-1 of wmap[r][u]*y[u][r][o]
+ * The sum runs in f32 in slot order, one fused multiply-add per slot, so the result is
+ * deterministic. Errors: NULL pointer; n_u, nb or out_dim < 1, nb*out_dim > 2^31 (SHAPE);
+ * a pointer not 4-byte aligned (ALIGN); launch failure.
+ */
+int q4mv_combine(const float *y, const float *wmap, float *out, int n_u, int nb, int out_dim,
+                 void *stream);
+
 /* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
    (two_row = 1) takes for this shape; a negative status if the shape is invalid. nb > 3
    runs on the MFMA kernel when its LDS footprint fits (see q4mv_path), else on the VALU

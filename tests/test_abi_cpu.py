@@ -29,6 +29,7 @@ def test_header_declares_expected_entry_points():
     fns = declared_functions()
     for name in ("q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_pack_codes", "q4mv_path",
                  "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_auto_path",
+                 "q4mv_quantize", "q4mv_experts", "q4mv_combine",
                  "q4mv_status_str", "q4mv_version"):
         assert name in fns
 
@@ -43,7 +44,7 @@ def test_status_strings(L):
     for st in (OK, ENULL, ESHAPE, EODD, EALIGN, ELAUNCH, EPATH, EVALUE):
         assert q.status_str(st) and q.status_str(st) != "unknown status"
     assert q.status_str(12345) == "unknown status"
-    assert L.q4mv_version() >= 200
+    assert L.q4mv_version() >= 300
 
 
 def gemv_args(**kw):
@@ -152,3 +153,40 @@ def test_quantize_validation(L):
     assert f(A + 4, A, A, A, 1, 64, None) == EALIGN
     assert f(A, A + 2, A, A, 1, 64, None) == EALIGN
     assert f(A, A, A + 1, A, 1, 64, None) == EALIGN
+
+
+def experts_args(**kw):
+    a = dict(w=A, s=A, b=A, n_bank=4, sel=A, n_sel=2, xe=A, xo=A, xsum=A, y=A, out=8, ind=128,
+             nb=1, shared=0, path=0)
+    a.update(kw)
+    return [a[k] for k in ("w", "s", "b", "n_bank", "sel", "n_sel", "xe", "xo", "xsum", "y",
+                           "out", "ind", "nb", "shared", "path")] + [None]
+
+
+def test_experts_validation(L):
+    f = L.q4mv_experts
+    for k in ("w", "s", "b", "sel", "xe", "xo", "xsum", "y"):
+        assert f(*experts_args(**{k: None})) == ENULL, k
+    for kw in (dict(n_bank=0), dict(n_sel=0), dict(n_sel=65536), dict(out=0), dict(ind=96),
+               dict(ind=32), dict(nb=0), dict(nb=17), dict(nb=16, ind=4160)):
+        assert f(*experts_args(**kw)) == ESHAPE, kw
+    for kw in (dict(w=A + 4), dict(sel=A + 2), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1),
+               dict(b=A + 1), dict(xsum=A + 2), dict(y=A + 1)):
+        assert f(*experts_args(**kw)) == EALIGN, kw
+    assert f(*experts_args(path=4)) == EPATH
+    assert f(*experts_args(path=-1)) == EPATH
+    assert f(*experts_args(path=2, out=7)) == EODD
+    # the MFMA path's LDS limit, as q4mv_path
+    assert f(*experts_args(path=3, nb=4, ind=16192)) == ESHAPE
+
+
+def test_combine_validation(L):
+    f = L.q4mv_combine
+    assert f(None, A, A, 2, 1, 8, None) == ENULL
+    assert f(A, None, A, 2, 1, 8, None) == ENULL
+    assert f(A, A, None, 2, 1, 8, None) == ENULL
+    for n_u, nb, out in ((0, 1, 8), (2, 0, 8), (2, 1, 0), (2, 65536, 65536)):
+        assert f(A, A, A, n_u, nb, out, None) == ESHAPE
+    assert f(A + 2, A, A, 2, 1, 8, None) == EALIGN
+    assert f(A, A + 1, A, 2, 1, 8, None) == EALIGN
+    assert f(A, A, A + 3, 2, 1, 8, None) == EALIGN
