@@ -16,6 +16,8 @@ never imports it.
 * :func:`silu`, :func:`gemv_silu`, :func:`swiglu` -- the fused epilogues of the same page:
   ``fn_qmv_silu_b`` stores silu(y / div), and ``fn_moe_act_b`` forms silu(gate) * up from the
   stacked gate/up output before the down projection's prep.
+* :func:`gemv_lowbit`, :func:`pack_lowbit` -- the Q2 / Q3 variants (dense double
+  reconstruction at the range midpoints; the packed layout the device reads).
 * :func:`experts`, :func:`combine` -- the selected-expert dispatch (a bank, expert ids,
   shared or per-expert activation rows) and the routing-weighted sum of the expert outputs.
 """
@@ -220,6 +222,66 @@ def combine(y, wmap):
         raise ValueError("y [n_u][nb][out] and wmap [nb][n_u] expected")
     terms = wmap.T[:, :, None] * y
     return terms.sum(axis=0), np.abs(terms).sum(axis=0)
+
+
+# Low-bit reconstruction w = (K q + M) s + b of fn_q2_rows_h / fn_q3_rows_h on the Constant
+# BATCH_MSL page: q is the 4-bit code's top `bits` bits (q4 >> 2, q4 >> 1), placed at the middle
+# of the range of 4-bit codes it stands for.
+LOWBIT_KM = {2: (4.0, 1.5), 3: (2.0, 0.5)}
+
+
+def _bf16_to_f64(bits):
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def gemv_lowbit(bits, codes, scales, biases, x, rows=None):
+    """Q2 / Q3 GEMV from 4-bit codes u8 [n_mat][out][in] (the low-bit code is q4 >> (4-bits)),
+    in double: y[m][r][o] = sum_i ((K q + M) S + B) x with (K, M) from LOWBIT_KM, and the
+    per-element bound sum_i |(K q + M) S x| + |B x|. rows: optional 1-D list of output rows
+    (then y and bound are [n_mat][nb][len(rows)])."""
+    k, mid = LOWBIT_KM[bits]
+    codes = np.asarray(codes)
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        codes, scales, biases = codes[:, rows], np.asarray(scales)[:, rows], \
+            np.asarray(biases)[:, rows]
+    q = (codes.astype(np.uint8) & 15) >> (4 - bits)
+    s = np.repeat(_bf16_to_f64(scales), GROUP, axis=2)
+    b = np.repeat(_bf16_to_f64(biases), GROUP, axis=2)
+    sq = (k * q.astype(np.float64) + mid) * s
+    xd = np.asarray(x, dtype=np.float32).astype(np.float64)
+    y = np.matmul(xd, np.transpose(sq + b, (0, 2, 1)))
+    bound = np.matmul(np.abs(xd), np.transpose(np.abs(sq) + np.abs(b), (0, 2, 1)))
+    return y, bound
+
+
+def pack_lowbit(bits, codes):
+    """The packed low-bit words of 4-bit codes u8 [n_rows][in] -> u32 [n_rows][in/32*bits].
+    Per 32-code chunk c, column t = 16i + 8u + p (i, u < 2, p < 8) holds q = q4 >> (4-bits):
+    Q2: q at bit (p < 4 ? 0 : 16) + 2(4u + p%4) of word 2c+i;
+    Q3: q >> 1 at that bit of word 2c+i, and q & 1 at bit (p < 4 ? 0 : 16) + 8u + 2(p%4) + i
+    of word 2C+c (C = in/32: the row's upper-bit words, then its lowest-bit words).
+    The placement puts each code where a mask lands it in the f16 lane of the activation pair
+    it multiplies (the masked casts of fn_q2_rows_h / fn_q3_rows_h)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    C = k // 32
+    q = ((codes & 15) >> (4 - bits)).astype(np.uint32).reshape(n, C, 32)
+    up = np.zeros((n, C, 2), dtype=np.uint32)
+    low = np.zeros((n, C), dtype=np.uint32)
+    for t in range(32):
+        i, u, p = t // 16, (t // 8) % 2, t % 8
+        half = 0 if p < 4 else 16
+        pos = half + 2 * (4 * u + p % 4)
+        if bits == 2:
+            up[:, :, i] |= q[:, :, t] << pos
+        else:
+            up[:, :, i] |= (q[:, :, t] >> 1) << pos
+            low |= (q[:, :, t] & 1) << (half + 8 * u + 2 * (p % 4) + i)
+    if bits == 2:
+        return up.reshape(n, 2 * C)
+    return np.concatenate([up.reshape(n, 2 * C), low], axis=1)
 
 
 def _bf16_rne_bits(x):

@@ -499,3 +499,86 @@ def test_combine_closed_forms(oracle_lib):
     out, mag = oracle_lib.combine(y, [[2.0, -1.0], [0.0, 0.5]])
     assert np.array_equal(out, [[-6.0, -5.0, -4.0], [4.5, 5.0, 5.5]])
     assert np.array_equal(mag, [[6.0, 9.0, 12.0], [4.5, 5.0, 5.5]])
+
+
+# ---- low-bit variants (Q2 / Q3)
+
+# (column within a 64-code row, word index, bit) written out by hand from the placement rule:
+# column t of chunk c meets activation pair (x_t, x_t+4) of its 8-column word, so columns
+# t and t+4 share one field position in the two 16-bit halves of a word.
+Q2_PROBES = [(0, 0, 0), (1, 0, 2), (3, 0, 6), (4, 0, 16), (7, 0, 22), (8, 0, 8), (11, 0, 14),
+             (12, 0, 24), (15, 0, 30), (16, 1, 0), (20, 1, 16), (24, 1, 8), (31, 1, 30),
+             (32, 2, 0), (45, 2, 26), (63, 3, 30)]
+# lowest-bit word of chunk c is word 2C + c (C = 2 here: words 4 and 5)
+Q3_LOW_PROBES = [(0, 4, 0), (4, 4, 16), (8, 4, 8), (13, 4, 26), (16, 4, 1), (20, 4, 17),
+                 (25, 4, 11), (31, 4, 31), (32, 5, 0), (63, 5, 31)]
+
+
+def test_lowbit_pack_probes(oracle_lib):
+    for col, word, bit in Q2_PROBES:
+        codes = np.zeros((1, 64), dtype=np.uint8)
+        codes[0, col] = 15
+        want = np.zeros(4, dtype=np.uint32)
+        want[word] = np.uint32(3) << bit
+        assert np.array_equal(oracle_lib.pack_lowbit(2, codes)[0], want), col
+        # Q3: the upper two bits at the Q2 position, the lowest bit in the low-bit word
+        codes[0, col] = 0b1110  # q3 = 7 -> upper 3, lowest 1
+        w3 = oracle_lib.pack_lowbit(3, codes)[0]
+        assert w3[word] == np.uint32(3) << bit and w3[1 - word % 2 + 2 * (word // 2)] == 0
+    for col, word, bit in Q3_LOW_PROBES:
+        codes = np.zeros((1, 64), dtype=np.uint8)
+        codes[0, col] = 0b0010  # q3 = 1: only the lowest bit
+        w3 = oracle_lib.pack_lowbit(3, codes)[0]
+        want = np.zeros(6, dtype=np.uint32)
+        want[word] = np.uint32(1) << bit
+        assert np.array_equal(w3, want), col
+    # only the top bits of the 4-bit code count, and every bit is used once
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, (5, 128), dtype=np.uint8)
+    for bits in (2, 3):
+        full = oracle_lib.pack_lowbit(bits, codes | 0xF0)
+        assert np.array_equal(full, oracle_lib.pack_lowbit(bits, codes))
+        ones = oracle_lib.pack_lowbit(bits, np.full((1, 128), 15, dtype=np.uint8))
+        assert np.all(ones == 0xFFFFFFFF)
+
+
+def test_lowbit_midpoints(oracle_lib):
+    """Each low-bit code stands for a range of 4-bit codes and is reconstructed at the mean
+    of that range: with S = 1, B = 0 and a one-hot x the output is that mean."""
+    for bits in (2, 3):
+        for q4 in range(16):
+            same = [v for v in range(16) if v >> (4 - bits) == q4 >> (4 - bits)]
+            codes = np.full((1, 1, 64), q4, dtype=np.uint8)
+            x = np.zeros((1, 1, 64), dtype=np.float32)
+            x[0, 0, 5] = 1.0
+            y, _ = oracle_lib.gemv_lowbit(bits, codes, np.full((1, 1, 1), ONE_BF16, np.uint16),
+                                          np.zeros((1, 1, 1), np.uint16), x)
+            assert y[0, 0, 0] == sum(same) / len(same), (bits, q4)
+
+
+def test_lowbit_decomposition(oracle_lib):
+    """y_lowbit = K * (GEMV of the low-bit codes, no bias) + M * (bias-only GEMV with S as the
+    bias) + (bias-only GEMV with B), each term from the C oracle, which shares no code with
+    gemv_lowbit; and the bound against a brute-force sum on a small case."""
+    case = workloads.make_shape(2, 24, 192, 3, seed=77)
+    zeros = np.zeros_like(case["codes"])
+    for bits in (2, 3):
+        K, M = oracle_lib.LOWBIT_KM[bits]
+        y, bound = oracle_lib.gemv_lowbit(bits, case["codes"], case["scales"], case["biases"],
+                                          case["x"])
+        q = case["codes"] >> (4 - bits)
+        t1, _ = oracle_lib.gemv(q, case["scales"], np.zeros_like(case["biases"]), case["x"])
+        t2, _ = oracle_lib.gemv(zeros, case["scales"], case["scales"], case["x"])
+        t3, _ = oracle_lib.gemv(zeros, case["scales"], case["biases"], case["x"])
+        assert np.allclose(y, K * t1 + M * t2 + t3, rtol=1e-12, atol=1e-12)
+        s = bf16_torch(case["scales"])
+        b = bf16_torch(case["biases"])
+        m, r, o = 1, 2, 17
+        brute = sum(abs((K * int(q[m, o, i]) + M) * s[m, o, i // 64] * float(case["x"][m, r, i]))
+                    + abs(b[m, o, i // 64] * float(case["x"][m, r, i])) for i in range(192))
+        assert bound[m, r, o] == pytest.approx(brute, rel=1e-12)
+    # selected rows agree with the full result
+    y, bound = oracle_lib.gemv_lowbit(3, case["codes"], case["scales"], case["biases"], case["x"])
+    ys, bs = oracle_lib.gemv_lowbit(3, case["codes"], case["scales"], case["biases"], case["x"],
+                                    rows=[23, 0, 5])
+    assert np.array_equal(ys, y[:, :, [23, 0, 5]]) and np.array_equal(bs, bound[:, :, [23, 0, 5]])
