@@ -57,6 +57,8 @@ def lib():
         L.q4mv_path_silu.argtypes = gemv + [f32, i32, p]
         L.q4mv_swiglu_prep.argtypes = [p, i32, i32, p, p, p, p]
         L.q4mv_quantize.argtypes = [p, p, p, p, i64, i32, p]
+        L.q4mv_pack_lowbit.argtypes = [i32, p, p, i64, i32, p]
+        L.q4mv_lowbit.argtypes = [i32] + [p] * 7 + [i32] * 5 + [p]
         L.q4mv_experts.argtypes = [p, p, p, i32, p, i32, p, p, p, p] + [i32] * 5 + [p]
         L.q4mv_combine.argtypes = [p, p, p, i32, i32, i32, p]
         L.q4mv_auto_path.argtypes = [i32, i32, i32, i32]
@@ -231,6 +233,47 @@ def q4mv_swiglu_prep(gu, xe=None, xo=None, xsum=None, stream=None):
                                                        xo.data_ptr(), xsum.data_ptr(),
                                                        _stream(gu, stream)))
     return xe, xo, xsum
+
+
+def q4mv_pack_lowbit(bits, codes, stream=None):
+    """4-bit codes uint8 [..., in_dim] -> the Q2 / Q3 packed words int32 [..., in_dim/32*bits]
+    (the low-bit code is the 4-bit code's top bits)."""
+    torch = _torch()
+    if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous():
+        raise ValueError("codes: contiguous uint8 GPU tensor expected")
+    in_dim = codes.shape[-1]
+    n_rows = codes.numel() // in_dim if in_dim else 0
+    w = torch.empty((*codes.shape[:-1], in_dim // 32 * int(bits)), dtype=torch.int32,
+                    device=codes.device)
+    _check("q4mv_pack_lowbit", lib().q4mv_pack_lowbit(int(bits), codes.data_ptr(), w.data_ptr(),
+                                                       n_rows, in_dim, _stream(codes, stream)))
+    return w
+
+
+def q4mv_lowbit(bits, w, scales, biases, xe, xo, xsum, nb, path=PATH_AUTO, y=None,
+                stream=None):
+    """Q2 / Q3 GEMV: w int32 [n_mat, out_dim, in_dim/32*bits] -> y f32 [n_mat, nb, out_dim]."""
+    torch = _torch()
+    if w.dim() != 3:
+        raise ValueError("w: expected [n_mat, out_dim, in_dim/32*bits]")
+    n_mat, out_dim, wpr = w.shape
+    if bits not in (2, 3) or wpr % bits:
+        raise ValueError("bits must be 2 or 3 and w's last dimension a multiple of it")
+    in_dim = wpr // bits * 32
+    _need(w, torch.int32, (n_mat, out_dim, wpr), "w")
+    _need(scales, torch.bfloat16, (n_mat, out_dim, in_dim // 64), "scales")
+    _need(biases, torch.bfloat16, (n_mat, out_dim, in_dim // 64), "biases")
+    _need(xe, torch.float16, (n_mat * nb, in_dim // 2), "xe")
+    _need(xo, torch.float16, (n_mat * nb, in_dim // 2), "xo")
+    _need(xsum, torch.float32, (n_mat * nb, in_dim // 32), "xsum")
+    if y is None:
+        y = torch.empty((n_mat, nb, out_dim), dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, (n_mat, nb, out_dim), "y")
+    _check("q4mv_lowbit", lib().q4mv_lowbit(
+        int(bits), w.data_ptr(), scales.data_ptr(), biases.data_ptr(), xe.data_ptr(),
+        xo.data_ptr(), xsum.data_ptr(), y.data_ptr(), n_mat, out_dim, in_dim, nb, int(path),
+        _stream(w, stream)))
+    return y
 
 
 def q4mv_experts(w, scales, biases, sel, xe, xo, xsum, nb, x_shared, path=PATH_AUTO, y=None,

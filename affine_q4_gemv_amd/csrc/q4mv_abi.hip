@@ -202,6 +202,42 @@ int q4mv_experts(const uint32_t *w, const uint16_t *scales, const uint16_t *bias
     return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
 }
 
+int q4mv_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows, int in_dim,
+                     void *stream)
+{
+    if (!codes || !w) return Q4MV_ERR_NULL;
+    if (bits != 2 && bits != 3) return Q4MV_ERR_VALUE;
+    if (n_rows < 1 || in_dim < 64 || in_dim % 64 != 0 ||
+        n_rows * (in_dim / 32) > (1LL << 31) - 256)
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(codes, 16) || !aligned(w, 4)) return Q4MV_ERR_ALIGN;
+    hipError_t e = launch_pack_lowbit(bits, codes, w, n_rows, in_dim,
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
+int q4mv_lowbit(int bits, const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+                int out_dim, int in_dim, int nb, int path, void *stream)
+{
+    if (!w || !scales || !biases || !xe || !xo || !xsum || !y) return Q4MV_ERR_NULL;
+    if (bits != 2 && bits != 3) return Q4MV_ERR_VALUE;
+    if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
+        nb > Q4MV_MAX_NB || (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(w, 8) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(scales, 2) ||
+        !aligned(biases, 2) || !aligned(xsum, 4) || !aligned(y, 4))
+        return Q4MV_ERR_ALIGN;
+    if (path < kAuto || path > kValu2) return Q4MV_ERR_PATH;
+    if (path == kAuto) path = (nb > 1 && out_dim % 2 == 0) ? kValu2 : kValu1;
+    if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
+    GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb, 0.0f,
+               static_cast<hipStream_t>(stream)};
+    a.bits = bits;
+    hipError_t e = launch_valu(a, path == kValu2 ? 2 : 1);
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
 int q4mv_combine(const float *y, const float *wmap, float *out, int n_u, int nb, int out_dim,
                  void *stream)
 {

@@ -23,6 +23,8 @@ struct GemvArgs {
     const int *sel = nullptr;
     int n_bank = 0;
     int x_shared = 0;
+    // Code width: 4 (affine-Q4), or the low-bit layouts 2 and 3 (VALU kernels only).
+    int bits = 4;
 };
 
 // Kernel paths (same numbering as q4mv_path in q4mv.h).
@@ -41,6 +43,8 @@ inline int valu_log2g(int in_dim)
 int auto_path(int in_dim, int nb, bool two_row, int out_dim);
 
 hipError_t launch_pack(const uint8_t *codes, uint32_t *w, int64_t n_codes, hipStream_t s);
+hipError_t launch_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows,
+                              int in_dim, hipStream_t s);
 hipError_t launch_combine(const float *y, const float *wmap, float *out, int n_u, int nb,
                           int out_dim, hipStream_t s);
 hipError_t launch_quantize(const float *wf, uint32_t *w, uint16_t *scales, uint16_t *biases,

@@ -22,6 +22,59 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint2 *__restrict
     w[i] = lo | (hi << 16);
 }
 
+// Low-bit pack (the stores behind fn_q2_rows_h / fn_q3_rows_h on the Constant BATCH_MSL page):
+// one thread per (row, 32-code chunk). The code kept is the 4-bit code's top BITS bits;
+// column 16i + 8u + p of the chunk (u < 2, p < 8) goes to bit (p < 4 ? 0 : 16) + 2(4u + p%4)
+// of word i (Q2 word, or Q3 upper-two-bit word), and for Q3 its lowest bit to bit
+// (p < 4 ? 0 : 16) + 8u + 2(p%4) + i of the chunk's lowest-bit word. Rows are C*BITS words:
+// Q2 2 words per chunk; Q3 the 2C upper words, then the C lowest-bit words.
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_lowbit_kernel(const uint4 *__restrict__ codes,
+                                                          uint32_t *__restrict__ w,
+                                                          int64_t n_chunks, int C)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_chunks) return;
+    const int64_t row = i / C;
+    const int c = (int)(i - row * C);
+    uint32_t b[8];
+    {
+        const uint4 v0 = codes[2 * i], v1 = codes[2 * i + 1];
+        b[0] = v0.x; b[1] = v0.y; b[2] = v0.z; b[3] = v0.w;
+        b[4] = v1.x; b[5] = v1.y; b[6] = v1.z; b[7] = v1.w;
+    }
+    uint32_t word[2] = {0u, 0u}, low = 0u;
+#pragma unroll
+    for (int col = 0; col < 32; col++) {
+        const uint32_t q4 = (b[col >> 2] >> (8 * (col & 3))) & 0xFu;
+        const uint32_t q = q4 >> (4 - BITS);
+        const int wi = col >> 4, u = (col >> 3) & 1, p = col & 7;
+        const int half = p < 4 ? 0 : 16;
+        if constexpr (BITS == 2) {
+            word[wi] |= q << (half + 2 * (4 * u + (p & 3)));
+        } else {
+            word[wi] |= (q >> 1) << (half + 2 * (4 * u + (p & 3)));
+            low |= (q & 1u) << (half + 8 * u + 2 * (p & 3) + wi);
+        }
+    }
+    uint32_t *wr = w + row * C * BITS;
+    wr[2 * c] = word[0];
+    wr[2 * c + 1] = word[1];
+    if constexpr (BITS == 3) wr[2 * C + c] = low;
+}
+
+hipError_t launch_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows,
+                              int in_dim, hipStream_t s)
+{
+    const int C = in_dim / 32;
+    const int64_t n_chunks = n_rows * C;
+    const int64_t blocks = (n_chunks + 255) / 256;
+    auto fn = bits == 2 ? pack_lowbit_kernel<2> : pack_lowbit_kernel<3>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const uint4 *>(codes), w, n_chunks, C);
+    return hipGetLastError();
+}
+
 // Activation prep. One thread per (row, even/odd pair k): x[2k], x[2k+1] -> f16 into
 // xe[k], xo[k]; the 16 threads of a 32-column chunk then sum their f16-rounded values.
 // in_dim % 64 == 0, so a chunk's 16 threads are one aligned 16-lane DPP row.

@@ -55,6 +55,7 @@ constexpr bool kValuXDirect = Q4MV_VALU_XDIRECT != 0;
 #ifndef Q4MV_VALU_NT
 #define Q4MV_VALU_NT 1
 #endif
+constexpr bool kValuNT = Q4MV_VALU_NT != 0;
 #ifndef Q4MV_VALU_XFIRST
 #define Q4MV_VALU_XFIRST 1
 #endif
@@ -65,9 +66,140 @@ constexpr bool kValuXDirect = Q4MV_VALU_XDIRECT != 0;
 #define Q4MV_VALU_PAIR_ROWS 2
 #endif
 
+// ---------------------------------------------------------------------------------------
+// Code widths. BITS = 4 is the affine-Q4 layout (one 16-byte chunk of 32 codes). BITS = 2 and
+// 3 are the low-bit variants of fn_q2_rows_h / fn_q3_rows_h (quantized_rows section of the
+// Constant BATCH_MSL page): the 4-bit code's top 2 or 3 bits, reconstructed at the middle of
+// the dropped range, w = (4q + 1.5) s + b and w = (2q + 0.5) s + b. A chunk of 32 codes is 2
+// words (Q2) or 2 + 1 words (Q3: upper-two-bit plane and lowest-bit plane); the layouts put
+// each code where a mask lands it in the f16 lane of the pair-layout activation it meets:
+//   Q2 word i of chunk c covers columns 32c+16i .. +15; column 32c+16i+8u+p (u < 2, p < 8)
+//      is the 2-bit field at bit (p < 4 ? 0 : 16) + 2*(4u + (p & 3)).
+//   Q3 upper words: the code's upper two bits at those positions; lowest-bit word of chunk c:
+//      the low bit of column 32c+16i+8u+p at bit (p < 4 ? 0 : 16) + 8u + 2*(p & 3) + i.
+// Row layout: Q4 C chunks of 4 words; Q2 C chunks of 2 words; Q3 the 2C upper words, then
+// the C lowest-bit words. So a row is C * BITS words in every case.
+
+// One chunk's code words of row base wr (u32 units), streamed with non-temporal loads
+// (each byte is used once). Q4: 4 words; Q2: 2 words (.x, .y); Q3: 2 upper words and the
+// lowest-bit word (.z).
+template <int BITS, bool NT>
+__device__ __forceinline__ uint4 load_chunk(const uint32_t *wr, int c, int C)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    if constexpr (BITS == 4) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(wr) + c;
+        const u32x4 v = NT ? __builtin_nontemporal_load(p) : *p;
+        return uint4{v[0], v[1], v[2], v[3]};
+    } else {
+        const u32x2 *p = reinterpret_cast<const u32x2 *>(wr) + c;
+        const u32x2 v = NT ? __builtin_nontemporal_load(p) : *p;
+        uint32_t lo = 0;
+        if constexpr (BITS == 3) {
+            const uint32_t *q = wr + 2 * C + c;
+            lo = NT ? __builtin_nontemporal_load(q) : *q;
+        }
+        return uint4{v[0], v[1], lo, 0u};
+    }
+}
+
+// Split one chunk into 16 f16 pairs: h[J][m] meets pair P_m of activation word J (pair
+// layout, x_unit). Q4: P0 and P2 come out as q*2^-24, P1 and P3 as 16q*2^-24. Q2 and Q3:
+// P_m comes out as 4^m q*2^-24.
+template <int BITS>
+__device__ __forceinline__ void split_chunk(const uint4 cw, uint32_t (&h)[4][4])
+{
+    if constexpr (BITS == 4) {
+        const uint32_t wd[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+        for (int J = 0; J < 4; J++) {
+            const uint32_t w8 = wd[J] >> 8;
+            h[J][0] = wd[J] & 0x000F000Fu;
+            h[J][1] = wd[J] & 0x00F000F0u;
+            h[J][2] = w8 & 0x000F000Fu;
+            h[J][3] = w8 & 0x00F000F0u;
+        }
+    } else if constexpr (BITS == 2) {
+        const uint32_t wd[2] = {cw.x, cw.y};
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const uint32_t w8 = wd[i] >> 8;
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                h[2 * i][m] = wd[i] & (0x00030003u << (2 * m));
+                h[2 * i + 1][m] = w8 & (0x00030003u << (2 * m));
+            }
+        }
+    } else {
+        // code = 2 * upper + lowest: the upper field moved up one bit, the lowest bit below it
+        const uint32_t wd[2] = {cw.x, cw.y};
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const uint32_t ua = wd[i] << 1, ub = wd[i] >> 7;
+            const uint32_t la = cw.z >> i, lb = cw.z >> (8 + i);
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                h[2 * i][m] = (ua & (0x00060006u << (2 * m))) | (la & (0x00010001u << (2 * m)));
+                h[2 * i + 1][m] =
+                    (ub & (0x00060006u << (2 * m))) | (lb & (0x00010001u << (2 * m)));
+            }
+        }
+    }
+}
+
+// sum(q * x) * 2^-24 of one chunk and one activation row from its split codes and the
+// row's four pair-layout units.
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const uint32_t (&h)[4][4], const uint4 (&xp)[4])
+{
+    if constexpr (BITS == 4) {
+        float ae = dot2_first(h[0][0], xp[0].x);
+        float ao = dot2_first(h[0][1], xp[0].y);
+        ae = dot2(h[0][2], xp[0].z, ae);
+        ao = dot2(h[0][3], xp[0].w, ao);
+#pragma unroll
+        for (int J = 1; J < 4; J++) {
+            ae = dot2(h[J][0], xp[J].x, ae);
+            ao = dot2(h[J][1], xp[J].y, ao);
+            ae = dot2(h[J][2], xp[J].z, ae);
+            ao = dot2(h[J][3], xp[J].w, ao);
+        }
+        return __builtin_fmaf(ao, 0.0625f, ae);
+    } else {
+        float a0 = dot2_first(h[0][0], xp[0].x);
+        float a1 = dot2_first(h[0][1], xp[0].y);
+        float a2 = dot2_first(h[0][2], xp[0].z);
+        float a3 = dot2_first(h[0][3], xp[0].w);
+#pragma unroll
+        for (int J = 1; J < 4; J++) {
+            a0 = dot2(h[J][0], xp[J].x, a0);
+            a1 = dot2(h[J][1], xp[J].y, a1);
+            a2 = dot2(h[J][2], xp[J].z, a2);
+            a3 = dot2(h[J][3], xp[J].w, a3);
+        }
+        return __builtin_fmaf(a3, 0.015625f, __builtin_fmaf(a2, 0.0625f, __builtin_fmaf(a1, 0.25f, a0)));
+    }
+}
+
+// acc += s' * qd + b' * xsum with (s', b') = (s, b) for Q4, (4s, 1.5s + b) for Q2 and
+// (2s, 0.5s + b) for Q3 (the chunk folds of fn_q4/q2/q3_rows_h).
+template <int BITS>
+__device__ __forceinline__ float chunk_fold(uint32_t sbits, uint32_t bbits, float qd, float xsv,
+                                            float acc)
+{
+    const float s = bf16_to_f32(sbits), b = bf16_to_f32(bbits);
+    if constexpr (BITS == 4) {
+        return __builtin_fmaf(s, qd, __builtin_fmaf(b, xsv, acc));
+    } else {
+        constexpr float kq = BITS == 2 ? 4.0f : 2.0f, km = BITS == 2 ? 1.5f : 0.5f;
+        return __builtin_fmaf(kq * s, qd, __builtin_fmaf(__builtin_fmaf(km, s, b), xsv, acc));
+    }
+}
+
 // LOG2G, CPL > 0: lane-group size and chunks per lane fixed at compile time (the common row
 // lengths); LOG2G = -1, CPL = 0: both taken at run time (any in_dim).
-template <int NB, int ROWS, int LOG2G, int CPL>
+template <int NB, int ROWS, int LOG2G, int CPL, int BITS>
 __global__ __launch_bounds__(kValuThreads) void valu_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
@@ -152,7 +284,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
         e = bad ? 0 : id;
         if (bad) epi_div = __builtin_nanf("");
     }
-    const uint4 *w_m = w + (size_t)e * out_dim * C;
+    const uint32_t *w_m = reinterpret_cast<const uint32_t *>(w) + (size_t)e * out_dim * C * BITS;
     const uint16_t *s_m = scales + (size_t)e * out_dim * groups;
     const uint16_t *b_m = biases + (size_t)e * out_dim * groups;
     float *y_m = y + ((size_t)m * nb_total + r0) * out_dim;
@@ -204,12 +336,12 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
         // in flight.
         auto load = [&](int ws, uint4 (&cw)[ROWS][CPL], uint32_t (&sv)[ROWS][CPL],
                         uint32_t (&bv)[ROWS][CPL]) {
-            const uint4 *wr[ROWS];
+            const uint32_t *wr[ROWS];
             const uint16_t *sr[ROWS], *br[ROWS];
 #pragma unroll
             for (int t = 0; t < ROWS; t++) {
                 const int row = min(ws * rows_per_wave + grp * ROWS + t, out_dim - 1);
-                wr[t] = w_m + (size_t)row * C;
+                wr[t] = w_m + (size_t)row * C * BITS;
                 sr[t] = s_m + (size_t)row * groups;
                 br[t] = b_m + (size_t)row * groups;
             }
@@ -218,18 +350,12 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                 const int c = j + (k << log2g);
 #pragma unroll
                 for (int t = 0; t < ROWS; t++) {
+                    cw[t][k] = load_chunk<BITS, kValuNT>(wr[t], c, C);
 #if Q4MV_VALU_NT
                     // streamed once: non-temporal loads (no reuse to keep in the caches)
-                    {
-                        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                        const u32x4 v = __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4 *>(wr[t] + c));
-                        cw[t][k] = uint4{v[0], v[1], v[2], v[3]};
-                    }
                     sv[t][k] = __builtin_nontemporal_load(sr[t] + (c >> 1));
                     bv[t][k] = __builtin_nontemporal_load(br[t] + (c >> 1));
 #else
-                    cw[t][k] = wr[t][c];
                     sv[t][k] = sr[t][c >> 1];
                     bv[t][k] = br[t][c >> 1];
 #endif
@@ -249,17 +375,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                 if constexpr (NB > 1 || ROWS > 1) asm volatile("" ::: "memory");
                 uint32_t h[ROWS][4][4];
 #pragma unroll
-                for (int t = 0; t < ROWS; t++) {
-                    const uint32_t wd[4] = {cc[t][k].x, cc[t][k].y, cc[t][k].z, cc[t][k].w};
-#pragma unroll
-                    for (int J = 0; J < 4; J++) {
-                        const uint32_t w8 = wd[J] >> 8;
-                        h[t][J][0] = wd[J] & 0x000F000Fu;
-                        h[t][J][1] = wd[J] & 0x00F000F0u;
-                        h[t][J][2] = w8 & 0x000F000Fu;
-                        h[t][J][3] = w8 & 0x00F000F0u;
-                    }
-                }
+                for (int t = 0; t < ROWS; t++) split_chunk<BITS>(cc[t][k], h[t]);
 #pragma unroll
                 for (int r = 0; r < NB; r++) {
                     uint4 xp[4];
@@ -274,23 +390,9 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                         xsv = xs[r * C + c];
                     }
 #pragma unroll
-                    for (int t = 0; t < ROWS; t++) {
-                        float ae = dot2_first(h[t][0][0], xp[0].x);
-                        float ao = dot2_first(h[t][0][1], xp[0].y);
-                        ae = dot2(h[t][0][2], xp[0].z, ae);
-                        ao = dot2(h[t][0][3], xp[0].w, ao);
-#pragma unroll
-                        for (int J = 1; J < 4; J++) {
-                            ae = dot2(h[t][J][0], xp[J].x, ae);
-                            ao = dot2(h[t][J][1], xp[J].y, ao);
-                            ae = dot2(h[t][J][2], xp[J].z, ae);
-                            ao = dot2(h[t][J][3], xp[J].w, ao);
-                        }
-                        const float qd = __builtin_fmaf(ao, 0.0625f, ae);
-                        acc[t][r] = __builtin_fmaf(bf16_to_f32(scb[t][k]), qd,
-                                                   __builtin_fmaf(bf16_to_f32(bcb[t][k]), xsv,
-                                                                  acc[t][r]));
-                    }
+                    for (int t = 0; t < ROWS; t++)
+                        acc[t][r] = chunk_fold<BITS>(scb[t][k], bcb[t][k],
+                                                     chunk_dot<BITS>(h[t], xp), xsv, acc[t][r]);
                 }
             }
             // all reductions first, then the stores (one divergent block at the very end)
@@ -387,7 +489,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                     for (int kk = 0; kk < 4; kk++) {
                         // clamped, unconditional loads (chunks past cpl are never used)
                         const int c = j + (min(k0 + kk, cpl - 1) << log2g);
-                        cc[t][kk] = w_m[(size_t)rowc[t] * C + c];
+                        cc[t][kk] = load_chunk<BITS, false>(w_m + (size_t)rowc[t] * C * BITS, c, C);
                         sc[t][kk] = s_m[(size_t)rowc[t] * groups + (c >> 1)];
                         bc[t][kk] = b_m[(size_t)rowc[t] * groups + (c >> 1)];
                     }
@@ -403,24 +505,10 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
                         const float xsv = xs[r * C + c];
 #pragma unroll
                         for (int t = 0; t < ROWS; t++) {
-                            const uint32_t wd[4] = {cc[t][kk].x, cc[t][kk].y, cc[t][kk].z,
-                                                    cc[t][kk].w};
-                            float ae = dot2_first(wd[0] & 0x000F000Fu, xp[0].x);
-                            float ao = dot2_first(wd[0] & 0x00F000F0u, xp[0].y);
-                            ae = dot2((wd[0] >> 8) & 0x000F000Fu, xp[0].z, ae);
-                            ao = dot2((wd[0] >> 8) & 0x00F000F0u, xp[0].w, ao);
-#pragma unroll
-                            for (int J = 1; J < 4; J++) {
-                                const uint32_t w8 = wd[J] >> 8;
-                                ae = dot2(wd[J] & 0x000F000Fu, xp[J].x, ae);
-                                ao = dot2(wd[J] & 0x00F000F0u, xp[J].y, ao);
-                                ae = dot2(w8 & 0x000F000Fu, xp[J].z, ae);
-                                ao = dot2(w8 & 0x00F000F0u, xp[J].w, ao);
-                            }
-                            const float qd = __builtin_fmaf(ao, 0.0625f, ae);
-                            acc[t][r] = __builtin_fmaf(bf16_to_f32(sc[t][kk]), qd,
-                                                       __builtin_fmaf(bf16_to_f32(bc[t][kk]),
-                                                                      xsv, acc[t][r]));
+                            uint32_t h[4][4];
+                            split_chunk<BITS>(cc[t][kk], h);
+                            acc[t][r] = chunk_fold<BITS>(sc[t][kk], bc[t][kk],
+                                                         chunk_dot<BITS>(h, xp), xsv, acc[t][r]);
                         }
                     }
                 }
@@ -453,40 +541,59 @@ typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const 
     X(6, 2) /* 4096 */ X(5, 5) /* 5120 */ X(6, 3) /* 6144 */ X(5, 7) /* 7168 */               \
     X(6, 4) /* 8192 */ X(6, 7) /* 14336 */
 
-// Whether (log2 G, CPL) is one of the specialised row lengths.
-static bool valu_specialised(int log2g, int cpl)
+// Low-bit codes: the expert row lengths only (640 and 2560); other lengths take the
+// generic kernel.
+#define Q4MV_LOWBIT_SHAPES(X) X(2, 5) /* 640 */ X(4, 5) /* 2560 */
+
+// Whether (log2 G, CPL) is one of the specialised row lengths of code width bits.
+static bool valu_specialised(int log2g, int cpl, int bits)
 {
 #define Q4MV_IS(L, K) \
     if (log2g == L && cpl == K) return true;
-    Q4MV_VALU_SHAPES(Q4MV_IS)
+    if (bits == 4) {
+        Q4MV_VALU_SHAPES(Q4MV_IS)
+    } else {
+        Q4MV_LOWBIT_SHAPES(Q4MV_IS)
+    }
 #undef Q4MV_IS
     return false;
 }
 
-template <int NB, int ROWS>
+template <int NB, int ROWS, int BITS>
 static ValuFn pick_shape(int log2g, int cpl)
 {
 #define Q4MV_PICK(L, K) \
-    if (log2g == L && cpl == K) return valu_kernel<NB, ROWS, L, K>;
-    Q4MV_VALU_SHAPES(Q4MV_PICK)
+    if (log2g == L && cpl == K) return valu_kernel<NB, ROWS, L, K, BITS>;
+    if constexpr (BITS == 4) {
+        Q4MV_VALU_SHAPES(Q4MV_PICK)
+    } else {
+        Q4MV_LOWBIT_SHAPES(Q4MV_PICK)
+    }
 #undef Q4MV_PICK
-    return valu_kernel<NB, ROWS, -1, 0>;
+    return valu_kernel<NB, ROWS, -1, 0, BITS>;
 }
 
-template <int ROWS>
+template <int ROWS, int BITS>
 static ValuFn pick_nb(int nb, int log2g, int cpl)
 {
     switch (nb) {
-    case 1: return pick_shape<1, ROWS>(log2g, cpl);
-    case 2: return pick_shape<2, ROWS>(log2g, cpl);
-    case 3: return pick_shape<3, ROWS>(log2g, cpl);
-    case 4: return pick_shape<4, ROWS>(log2g, cpl);
+    case 1: return pick_shape<1, ROWS, BITS>(log2g, cpl);
+    case 2: return pick_shape<2, ROWS, BITS>(log2g, cpl);
+    case 3: return pick_shape<3, ROWS, BITS>(log2g, cpl);
+    case 4: return pick_shape<4, ROWS, BITS>(log2g, cpl);
     // larger batches: generic kernel (the MFMA kernel is the fast path there)
-    case 5: return valu_kernel<5, ROWS, -1, 0>;
-    case 6: return valu_kernel<6, ROWS, -1, 0>;
-    case 7: return valu_kernel<7, ROWS, -1, 0>;
-    default: return valu_kernel<8, ROWS, -1, 0>;
+    case 5: return valu_kernel<5, ROWS, -1, 0, BITS>;
+    case 6: return valu_kernel<6, ROWS, -1, 0, BITS>;
+    case 7: return valu_kernel<7, ROWS, -1, 0, BITS>;
+    default: return valu_kernel<8, ROWS, -1, 0, BITS>;
     }
+}
+
+template <int BITS>
+static ValuFn pick(int rows, int nb, int log2g, int cpl)
+{
+    return rows == 1 ? pick_nb<1, BITS>(nb, log2g, cpl)
+                     : pick_nb<Q4MV_VALU_PAIR_ROWS, BITS>(nb, log2g, cpl);
 }
 
 static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
@@ -495,10 +602,12 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const int C = a.in_dim / 32;
     const int cpl = C >> log2g;
     if (rows == 2) rows = Q4MV_VALU_PAIR_ROWS;
-    ValuFn fn = rows == 1 ? pick_nb<1>(nbp, log2g, cpl) : pick_nb<Q4MV_VALU_PAIR_ROWS>(nbp, log2g, cpl);
+    ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl)
+                : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl)
+                              : pick<4>(rows, nbp, log2g, cpl);
     // activations straight into registers need no LDS (same rule as the kernel's XREG; the
     // generic kernel and NB > 4 always stage)
-    const bool xdirect = kValuXDirect && nbp <= 4 && valu_specialised(log2g, cpl) &&
+    const bool xdirect = kValuXDirect && nbp <= 4 && valu_specialised(log2g, cpl, a.bits) &&
                          nbp * cpl <= Q4MV_VALU_XREG_MAX;
     const size_t lds = xdirect ? 0 : (size_t)nbp * C * 64 + (size_t)nbp * C * 4;
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);

@@ -69,7 +69,7 @@ def load_traffic(workload, nb, kernel):
 class Problem:
     """Device buffers of one workload: R rotated weight copies, activations and outputs."""
 
-    def __init__(self, name, nb, rotate=True, silu_div=None):
+    def __init__(self, name, nb, rotate=True, silu_div=None, bits=4):
         import numpy as np
         import torch
 
@@ -78,13 +78,17 @@ class Problem:
 
         self.q4, self.torch = q4, torch
         self.silu_div = silu_div
+        self.bits = bits
         c = workloads.make_case(name, nb=nb)
         self.name = name
         self.n_mat, self.out_dim, self.in_dim, self.nb = c["n_mat"], c["out_dim"], c["in_dim"], nb
         self.weight_bytes = workloads.weight_bytes(self.n_mat, self.out_dim, self.in_dim)
+        if bits != 4:  # code bytes scale with the width; scales and biases do not
+            self.weight_bytes = self.n_mat * self.out_dim * (
+                self.in_dim // 32 * 4 * bits + self.in_dim // 64 * 4)
         dev = torch.device("cuda:0")
         codes = torch.from_numpy(c["codes"]).to(dev)
-        w0 = q4.q4mv_pack_codes(codes)
+        w0 = q4.q4mv_pack_codes(codes) if bits == 4 else q4.q4mv_pack_lowbit(bits, codes)
         del codes
 
         def bf16(bits):
@@ -120,7 +124,10 @@ class Problem:
 
     def gemv(self, i):
         k = i % self.R
-        if self.silu_div is not None:
+        if self.bits != 4:
+            self.q4.q4mv_lowbit(self.bits, self.w[k], self.s[k], self.b[k], self.xe, self.xo,
+                                self.xsum, self.nb, y=self.y)
+        elif self.silu_div is not None:
             self.q4.q4mv_silu(self.w[k], self.s[k], self.b[k], self.xe, self.xo, self.xsum,
                               self.nb, self.silu_div, y=self.y)
         else:
@@ -544,6 +551,25 @@ def main():
         ms = p.time_kernel(200)
         gbps = p.weight_bytes / (ms * 1e-3) / 1e9
         sweep.append({"workload": "lm_head", "nb": 1, "epilogue": "silu(y/2)",
+                      "kernel_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
+                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1), "path": p.path})
+        del p
+        # the Q2 / Q3 variants (VALU kernels), next to Q4 at the same shape and batch
+        for name, nb in (("lm_head", 1), ("lm_head", 4), ("moe_down", 2), ("up", 1)):
+            for bits in (2, 3):
+                p = Problem(name, nb, bits=bits)
+                ms = p.time_kernel(200)
+                gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+                sweep.append({"workload": name, "nb": nb, "codes": f"Q{bits}",
+                              "kernel_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
+                              "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+                              "rows_per_s": round(p.n_mat * p.out_dim / (ms * 1e-3), 1)})
+                del p
+                torch.cuda.empty_cache()
+        p = Problem("moe_down", 2)
+        ms = p.time_kernel(200)
+        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+        sweep.append({"workload": "moe_down", "nb": 2, "codes": "Q4",
                       "kernel_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
                       "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1), "path": p.path})
         del p

@@ -178,6 +178,44 @@ int q4mv_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo,
                      void *stream);
 
 /*
+ * q4mv_pack_lowbit -- pack 4-bit codes into the Q2 (bits = 2) or Q3 (bits = 3) layout.
+ *
+ * The low-bit code is the 4-bit code's top bits, q = q4 >> (4 - bits), as fn_q2_rows_h and
+ * fn_q3_rows_h on the Constant BATCH_MSL page define them (codes q4 >> 2 and q4 >> 1). Each
+ * 32-code chunk c of a row holds column t = 16i + 8u + p (i, u < 2, p < 8):
+ *   Q2: q at bit (p < 4 ? 0 : 16) + 2(4u + p%4) of word 2c + i (2 words per chunk);
+ *   Q3: q >> 1 at that bit of word 2c + i, and q & 1 at bit (p < 4 ? 0 : 16) + 8u + 2(p%4) + i
+ *       of word 2C + c, C = in_dim/32 (a row is its 2C upper-bit words, then its C
+ *       lowest-bit words: the two planes of fn_q3_rows_h).
+ * A row is C*bits words. (The placement puts each code in the f16 lane of the activation
+ * pair it multiplies, like the masked casts of those kernels.)
+ *   codes : u8  [n_rows][in_dim]          one 4-bit code per byte (bits 4..7 ignored)
+ *   w     : u32 [n_rows][in_dim/32*bits]  output (n_rows = n_mat * out_dim)
+ * Errors: NULL pointer; bits not 2 or 3 (VALUE); n_rows < 1, in_dim < 64, in_dim % 64 != 0,
+ * n_rows*in_dim/32 >= 2^31 - 256 (SHAPE); codes not 16-byte or w not 4-byte aligned (ALIGN).
+ */
+int q4mv_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows, int in_dim,
+                     void *stream);
+
+/*
+ * q4mv_lowbit -- the Q2 / Q3 GEMV (fn_q2_rows_h, fn_q3_rows_h on the Constant BATCH_MSL
+ * page): each weight is reconstructed at the middle of the 4-bit codes its code stands for,
+ *   Q2: w = (4q + 1.5) s + b,   Q3: w = (2q + 0.5) s + b,
+ * with the scale s and bias b of the 64-wide group (the same bf16 arrays as q4mv), so per
+ * 32-code chunk acc += K s sum(q x) + (M s + b) sum(x). Same arguments, layouts and
+ * accumulation as q4mv except:
+ *   bits : 2 or 3;  w : u32 [n_mat][out_dim][in_dim/32*bits] (q4mv_pack_lowbit layout)
+ *   path : 0 automatic (1 for nb = 1 or odd out_dim, else 2), 1 one row per lane group,
+ *          2 two rows per lane group (out_dim even). The two give bitwise the same result.
+ * The matrix-core kernel is not offered for these widths.
+ * Errors: as q4mv (w 8-byte aligned), plus VALUE for bits, PATH for a path outside 0..2,
+ * ODD_ROWS for path 2 with odd out_dim.
+ */
+int q4mv_lowbit(int bits, const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
+                int out_dim, int in_dim, int nb, int path, void *stream);
+
+/*
  * q4mv_experts -- the GEMV over selected matrices of a bank (the selected-expert launch
  * launch_qmatvec_bf16w_sel on the qwen4exp_gpu.rs page: a bank, a device array of expert
  * ids and an activation stride that may be 0; and the unique-expert dispatch of

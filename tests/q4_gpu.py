@@ -5,8 +5,13 @@ import torch
 
 import affine_q4_gemv_amd as q4
 
-REL_L2 = 1e-3       # relative L2 error over all outputs
+REL_L2 = 1e-3       # relative L2 error over all outputs (results of REL_L2_MIN_N values or more)
 ELEM = 2e-3         # per element: |err| <= ELEM * sum_i(|S q x| + |B x|)
+# The relative L2 error is an aggregate: over a handful of outputs it is the relative error of
+# single values, which cancellation in y (W has mean about 0) makes arbitrarily large while the
+# error itself stays within the per-element bound. Below this many outputs only the
+# per-element bound applies.
+REL_L2_MIN_N = 64
 
 
 def dev():
@@ -51,8 +56,9 @@ def parity(y_gpu, y_ref, bound, what=""):
     nref = np.linalg.norm(y_ref)
     rel = np.linalg.norm(err) / nref if nref > 0 else np.linalg.norm(err)
     ratio = np.max(err / (ELEM * bound + 1e-300)) if err.size else 0.0
-    assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
     assert ratio <= 1.0, f"{what}: per-element error {ratio:.3f}x the bound"
+    if y_gpu.size >= REL_L2_MIN_N:
+        assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
     return rel, ratio
 
 

@@ -29,7 +29,8 @@ def test_header_declares_expected_entry_points():
     fns = declared_functions()
     for name in ("q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_pack_codes", "q4mv_path",
                  "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_auto_path",
-                 "q4mv_quantize", "q4mv_experts", "q4mv_combine",
+                 "q4mv_quantize", "q4mv_experts", "q4mv_combine", "q4mv_pack_lowbit",
+                 "q4mv_lowbit",
                  "q4mv_status_str", "q4mv_version"):
         assert name in fns
 
@@ -190,3 +191,30 @@ def test_combine_validation(L):
     assert f(A + 2, A, A, 2, 1, 8, None) == EALIGN
     assert f(A, A + 1, A, 2, 1, 8, None) == EALIGN
     assert f(A, A, A + 3, 2, 1, 8, None) == EALIGN
+
+
+def test_lowbit_validation(L):
+    f = L.q4mv_lowbit
+    for bits in (2, 3):
+        for k in ("w", "s", "b", "xe", "xo", "xsum", "y"):
+            assert f(bits, *gemv_args(**{k: None}), 0, None) == ENULL, k
+        for kw in (dict(n_mat=0), dict(out=0), dict(ind=96), dict(ind=32), dict(nb=0),
+                   dict(nb=17), dict(nb=16, ind=4160)):
+            assert f(bits, *gemv_args(**kw), 0, None) == ESHAPE, kw
+        for kw in (dict(w=A + 4), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1), dict(xsum=A + 2),
+                   dict(y=A + 1)):
+            assert f(bits, *gemv_args(**kw), 0, None) == EALIGN, kw
+        assert f(bits, *gemv_args(), 3, None) == EPATH   # no matrix-core kernel
+        assert f(bits, *gemv_args(), -1, None) == EPATH
+        assert f(bits, *gemv_args(out=7), 2, None) == EODD
+    for bits in (1, 4, 0):
+        assert f(bits, *gemv_args(), 0, None) == EVALUE
+    g = L.q4mv_pack_lowbit
+    assert g(2, None, A, 1, 64, None) == ENULL
+    assert g(3, A, None, 1, 64, None) == ENULL
+    assert g(4, A, A, 1, 64, None) == EVALUE
+    assert g(2, A, A, 0, 64, None) == ESHAPE
+    assert g(2, A, A, 1, 96, None) == ESHAPE
+    assert g(3, A, A, 1 << 26, 2048, None) == ESHAPE
+    assert g(2, A + 8, A, 1, 64, None) == EALIGN
+    assert g(3, A, A + 2, 1, 64, None) == EALIGN
