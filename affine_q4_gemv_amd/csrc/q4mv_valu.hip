@@ -62,6 +62,17 @@ constexpr bool kValuNT = Q4MV_VALU_NT != 0;
 #ifndef Q4MV_VALU_BALANCE
 #define Q4MV_VALU_BALANCE 0
 #endif
+// Low-bit widths: persistent blocks per CU of the one-row kernel, a floor on waves per SIMD
+// (caps registers), and the next step's loads issued before the current step's compute.
+#ifndef Q4MV_LOWBIT1_BLOCKS_PER_CU
+#define Q4MV_LOWBIT1_BLOCKS_PER_CU 4
+#endif
+#ifndef Q4MV_LOWBIT_MIN_WAVES
+#define Q4MV_LOWBIT_MIN_WAVES 1
+#endif
+#ifndef Q4MV_LOWBIT_PREFETCH
+#define Q4MV_LOWBIT_PREFETCH 0
+#endif
 #ifndef Q4MV_VALU_PAIR_ROWS
 #define Q4MV_VALU_PAIR_ROWS 2
 #endif
@@ -200,7 +211,7 @@ __device__ __forceinline__ float chunk_fold(uint32_t sbits, uint32_t bbits, floa
 // LOG2G, CPL > 0: lane-group size and chunks per lane fixed at compile time (the common row
 // lengths); LOG2G = -1, CPL = 0: both taken at run time (any in_dim).
 template <int NB, int ROWS, int LOG2G, int CPL, int BITS>
-__global__ __launch_bounds__(kValuThreads) void valu_kernel(
+__global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES) void valu_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
@@ -414,7 +425,7 @@ __global__ __launch_bounds__(kValuThreads) void valu_kernel(
             }
         };
         int ws = blockIdx.x * (kValuThreads / 64) + (threadIdx.x >> 6);
-        if constexpr (kValuPrefetch) {
+        if constexpr (BITS == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0) {
             // next step's codes are in flight while this step computes
             uint4 cn[ROWS][CPL];
             uint32_t sn[ROWS][CPL], bn[ROWS][CPL];
@@ -616,7 +627,9 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const long wave_steps = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
     const long blocks_needed = (wave_steps + 3) / 4;
     // persistent blocks: enough to fill every CU a few times over, shared by the matrices
-    const long per_cu = std::min<long>(rows == 1 ? Q4MV_VALU1_BLOCKS_PER_CU : Q4MV_VALU_BLOCKS_PER_CU,
+    const long per_cu = std::min<long>(rows != 1      ? Q4MV_VALU_BLOCKS_PER_CU
+                                       : a.bits == 4 ? Q4MV_VALU1_BLOCKS_PER_CU
+                                                     : Q4MV_LOWBIT1_BLOCKS_PER_CU,
                                        resident_blocks(reinterpret_cast<const void *>(fn),
                                                        kValuThreads, lds));
     const long cap = std::max(1L, (long)device_cus() * per_cu / a.n_mat);
