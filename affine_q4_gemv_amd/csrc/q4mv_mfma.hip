@@ -18,14 +18,18 @@
 //
 // Loads: a wave's work unit is (tile, quad) = 32 rows x 4 scale groups (128 bytes of codes
 // per row). It is read from HBM as whole 128-byte lines (8 lanes per row, 8 rows per load
-// instruction) plus one 8-byte scale and bias load per row, written to a per-wave LDS
-// scratch, and read back in the MFMA operand layout; the next unit's loads are issued right
-// after the scratch writes, so they are in flight while the current unit computes.
+// instruction), written to a per-wave LDS scratch, and read back in the MFMA operand layout;
+// the next unit's loads are issued right after the scratch writes, so they are in flight
+// while the current unit computes. Scales and biases (lanes 0..31 a row's scales, 32..63
+// its biases) are the costly part of the load stream: each lane reads a different row, so
+// one instruction touches dozens of cache lines. Where the layout allows, one 16-byte load
+// covers two quads and is made only by the unit that starts the pair; else 8 bytes per unit.
 //
-// Work split: KS waves (a tile group) share one 32-row tile, each taking a contiguous range
-// of the row's quads; with KS > 1 their partial sums meet in LDS and are added in a fixed
-// order (part 0 + 1 + ...), so results do not depend on the grid. A block holds WPB / KS
-// tile groups and strides over tiles.
+// Work split: KS waves (a tile group) share one 32-row tile; with KS > 2 they take
+// interleaved quads (wave q: q, q+KS, ...), so at each step they read adjacent pieces of
+// every row, else contiguous ranges (which the paired scale loads need). Their partial sums
+// meet in LDS and are added in a fixed order (part 0 + 1 + ...), so results do not depend
+// on the grid. A block holds WPB / KS tile groups and strides over tiles.
 #include "q4mv_device.h"
 #include "q4mv_internal.h"
 
@@ -45,11 +49,22 @@
 #ifndef Q4MV_MFMA_NT
 #define Q4MV_MFMA_NT 1
 #endif
-#ifndef Q4MV_MFMA_SB_COMPACT
-#define Q4MV_MFMA_SB_COMPACT 0
-#endif
 #ifndef Q4MV_MFMA_BALANCE
 #define Q4MV_MFMA_BALANCE 0
+#endif
+// The KS waves of a tile take interleaved quads (wave q: q, q+KS, ...) instead of
+// contiguous ranges when the scale loads are not paired (measured faster for small tile
+// counts).
+#ifndef Q4MV_MFMA_INTERLEAVE
+#define Q4MV_MFMA_INTERLEAVE 1
+#endif
+// 16-byte scale and bias loads (one per two quads) where the layout allows and the K-split
+// is at most SB16_MAX_KS.
+#ifndef Q4MV_MFMA_SB16
+#define Q4MV_MFMA_SB16 1
+#endif
+#ifndef Q4MV_MFMA_SB16_MAX_KS
+#define Q4MV_MFMA_SB16_MAX_KS 2
 #endif
 #ifndef Q4MV_MFMA_BLOCKS_PER_CU
 #define Q4MV_MFMA_BLOCKS_PER_CU 4
@@ -60,17 +75,21 @@ namespace q4mv_impl {
 // Waves per block: 8 (two per SIMD), or 4 when the LDS of 8 does not fit.
 constexpr int kMfmaWaves = 8;
 // Per-wave LDS scratch of one unit: codes 32 rows x 128 B, then scales and biases
-// 2 x 32 rows x 8 B (in 16-byte units).
+// 2 x 32 rows x 8 B, or x 16 B with 16-byte scale loads (in 16-byte units).
 constexpr int kScratchUnits = 32 * 8 + 32;
+constexpr int scratch_units(int sbw) { return 32 * 8 + (sbw == 16 ? 64 : 32); }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // A unit's scales and biases in flight: two dwords (one 8-byte load per lane) or four
 // 2-byte values (compact loads).
 struct SbRegs { uint32_t v[4]; };
 
 // WPB: waves per block. KS: waves per tile (K-split). NB16: activation rows 8..15 are live
-// (nb > 8). SB8: scales and biases of a quad are one aligned 8-byte load (groups % 4 == 0
-// and 8-byte aligned arrays); else four 2-byte loads with clamped indices.
-template <int WPB, int KS, bool NB16, bool SB8>
+// (nb > 8). SBW: how a lane loads its row's scales (lanes 0..31) or biases (32..63):
+// 16 = one aligned 16-byte load for two quads, made by the unit of the even quad (or the
+// first unit of a part) and kept in the scratch for the next (groups % 8 == 0, 16-byte
+// aligned arrays; halves the scattered scale loads); 8 = one aligned 8-byte load per quad
+// (groups % 4 == 0, 8-byte aligned); 2 = four 2-byte loads with clamped indices.
+template <int WPB, int KS, bool NB16, int SBW>
 __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
@@ -157,8 +176,11 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // largest part, so it is the same for every wave of the block and every wave meets the
     // per-tile barrier equally often (units past a wave's part are computed with zero
     // scales and biases)
-    const int q_begin = quarter * quads / KS;
-    const int q_end = (quarter + 1) * quads / KS;
+    // (16-byte scale loads pair consecutive quads, so they keep contiguous parts)
+    constexpr bool kInterleave = Q4MV_MFMA_INTERLEAVE && SBW != 16;
+    const int q_begin = kInterleave ? quarter : quarter * quads / KS;
+    const int q_step = kInterleave ? KS : 1;
+    const int q_end = kInterleave ? quads : (quarter + 1) * quads / KS;
     const int nunit = (quads + KS - 1) / KS;
     const int tiles = (out_dim + 31) >> 5;
     const int tstride = gridDim.x * TPB;
@@ -189,7 +211,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const int lr8 = lane >> 3, lc = lane & 7;
     const int sbrow = narrow ? min(lane & 31, out_dim - 1) : (lane & 31);
     const uint16_t *const sb_m = lane < 32 ? s_m : b_m;
-    auto load = [&](int tile, int qd, u32x4 (&cw)[4], SbRegs &sb) {
+    auto load = [&](int tile, int qd, int u, u32x4 (&cw)[4], SbRegs &sb) {
         const int trow = tile_row(tile);
         const int chunk = min(8 * qd + lc, C - 1);
 #pragma unroll
@@ -203,19 +225,17 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
             cw[r] = reinterpret_cast<const u32x4 *>(w_m)[(size_t)(trow + row) * C + chunk];
 #endif
         }
-#if Q4MV_MFMA_SB_COMPACT
-        // four 2-byte loads per lane: load i covers the scales (i < 2) or biases of rows
-        // 16*(i&1) .. +15, four consecutive lanes reading one row's four groups
-        const int g = min(4 * qd + (lane & 3), groups - 1);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int row = 16 * (i & 1) + (lane >> 2);
-            const int rr = narrow ? min(row, out_dim - 1) : row;
-            sb.v[i] = (i < 2 ? s_m : b_m)[(size_t)(trow + rr) * groups + g];
-        }
-#else
         const uint16_t *srow = sb_m + (size_t)(trow + sbrow) * groups;
-        if constexpr (SB8) {
+        if constexpr (SBW == 16) {
+            // only units that start a pair load (measured faster than a dummy load)
+            if ((qd & 1) == 0 || u == 0) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(srow + 4 * (qd & ~1));
+                sb.v[0] = v.x;
+                sb.v[1] = v.y;
+                sb.v[2] = v.z;
+                sb.v[3] = v.w;
+            }
+        } else if constexpr (SBW == 8) {
             const uint2 v = *reinterpret_cast<const uint2 *>(srow + 4 * qd);
             sb.v[0] = v.x;
             sb.v[1] = v.y;
@@ -226,27 +246,24 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
             sb.v[0] = v[0] | (v[1] << 16);
             sb.v[1] = v[2] | (v[3] << 16);
         }
-#endif
     };
     // This wave's scratch: codes of row r, chunk slot c at r*8 + (c ^ (r & 7)) (the XOR
     // keeps both the row-major writes and the MFMA-layout reads free of bank conflicts),
-    // then scales of rows 0..31 and biases of rows 0..31 as 8-byte entries.
-    uint4 *const scratch = scratch_all + wv * kScratchUnits;
+    // then scales of rows 0..31 and biases of rows 0..31 as 8-byte (16-byte) entries.
+    uint4 *const scratch = scratch_all + wv * scratch_units(SBW);
     uint2 *const sbs = reinterpret_cast<uint2 *>(scratch + 32 * 8);
-    auto put = [&](const u32x4 (&cw)[4], const SbRegs &sb) {
+    auto put = [&](const u32x4 (&cw)[4], const SbRegs &sb, int qd, int u) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = 8 * r + lr8;
             reinterpret_cast<u32x4 *>(scratch)[row * 8 + (lc ^ (row & 7))] = cw[r];
         }
-#if Q4MV_MFMA_SB_COMPACT
-        uint16_t *const sbs16 = reinterpret_cast<uint16_t *>(sbs);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            sbs16[((i >> 1) * 32 + 16 * (i & 1) + (lane >> 2)) * 4 + (lane & 3)] = (uint16_t)sb.v[i];
-#else
-        sbs[lane] = uint2{sb.v[0], sb.v[1]};
-#endif
+        if constexpr (SBW == 16) {
+            if ((qd & 1) == 0 || u == 0)
+                reinterpret_cast<uint4 *>(sbs)[lane] = uint4{sb.v[0], sb.v[1], sb.v[2], sb.v[3]};
+        } else {
+            sbs[lane] = uint2{sb.v[0], sb.v[1]};
+        }
     };
 
     // this lane's activation row in LDS (row nb - 1 past nb), offset to its chunk parity
@@ -259,7 +276,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     int base = blockIdx.x * TPB;
     int ui = 0;  // unit of the current tile
     int step = 0;
-    auto unit_quad = [&](int u) { return min(q_begin + u, quads - 1); };
+    auto unit_quad = [&](int u) { return min(q_begin + q_step * u, quads - 1); };
 
     // Loads run two units ahead: (abase, aui) is the unit the next load fetches, and the
     // two register sets alternate (the loop is unrolled by two so each set is static).
@@ -274,25 +291,26 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     };
     u32x4 c0[4], c1[4];
     SbRegs s0, s1;
-    if (more(abase)) load(abase + slot, unit_quad(aui), c0, s0);
+    if (more(abase)) load(abase + slot, unit_quad(aui), aui, c0, s0);
     advance(abase, aui);
-    if (more(abase)) load(abase + slot, unit_quad(aui), c1, s1);
+    if (more(abase)) load(abase + slot, unit_quad(aui), aui, c1, s1);
     advance(abase, aui);
     stage();  // every wave joins the staging barrier exactly once
     if (!more(base)) return;
     auto step_unit = [&](u32x4 (&cc)[4], SbRegs &sb) {
         const int tile = base + slot;
-        const int qd = q_begin + ui;  // may be past this wave's part: then all masked
+        const int qd = q_begin + q_step * ui;  // may be past this wave's part: then masked
         const bool last = ui + 1 == nunit;
-        put(cc, sb);  // waits for this unit's loads
-        if (more(abase)) load(abase + slot, unit_quad(aui), cc, sb);
+        const int qx = min(qd, quads - 1);
+        put(cc, sb, qx, ui);  // waits for this unit's loads
+        if (more(abase)) load(abase + slot, unit_quad(aui), aui, cc, sb);
         advance(abase, aui);
         if (ui == 0) {
 #pragma unroll
             for (int i = 0; i < NACC; i++) acc[i] = 0.0f;
         }
-        const uint2 s4 = sbs[n], b4 = sbs[32 + n];
-        const int qx = min(qd, quads - 1);
+        const uint2 s4 = SBW == 16 ? sbs[2 * n + (qx & 1)] : sbs[n];
+        const uint2 b4 = SBW == 16 ? sbs[2 * (32 + n) + (qx & 1)] : sbs[32 + n];
 #pragma unroll
         for (int g4 = 0; g4 < 4; g4++) {
             const int g = 4 * qx + g4;
@@ -370,11 +388,18 @@ typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const 
                        const uint2 *, const float *, float *, int, int, int, float,
                        const int *, int, int);
 
-template <int WPB, int KS>
-static MfmaFn pick(bool nb16, bool sb8)
+template <int WPB, int KS, bool NB16>
+static MfmaFn pick_sb(int sbw)
 {
-    if (nb16) return sb8 ? mfma_kernel<WPB, KS, true, true> : mfma_kernel<WPB, KS, true, false>;
-    return sb8 ? mfma_kernel<WPB, KS, false, true> : mfma_kernel<WPB, KS, false, false>;
+    return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16>
+           : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8>
+                      : mfma_kernel<WPB, KS, NB16, 2>;
+}
+
+template <int WPB, int KS>
+static MfmaFn pick(bool nb16, int sbw)
+{
+    return nb16 ? pick_sb<WPB, KS, true>(sbw) : pick_sb<WPB, KS, false>(sbw);
 }
 
 static int mfma_ks(long tiles, int quads)
@@ -405,20 +430,24 @@ hipError_t launch_mfma(const GemvArgs &a)
     const long tiles = (a.out_dim + 31) / 32;
     const MfmaShape sh = mfma_shape(a.in_dim, a.nb, tiles * a.n_mat);
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
-    const size_t lds = mfma_lds_bytes(a.in_dim, a.nb) + mfma_part_bytes(sh.wpb, sh.ks, nb16) +
-                       (size_t)sh.wpb * kScratchUnits * 16;
-    // (with an expert table the scale addresses are not known on the host: 2-byte loads)
-    const bool sb8 = groups % 4 == 0 && (uintptr_t)a.scales % 8 == 0 &&
-                     (uintptr_t)a.biases % 8 == 0;
+    const size_t lds0 = mfma_lds_bytes(a.in_dim, a.nb) + mfma_part_bytes(sh.wpb, sh.ks, nb16);
+    // 16-byte scale loads when the layout allows and their larger scratch still fits
+    int sbw = groups % 4 == 0 && (uintptr_t)a.scales % 8 == 0 && (uintptr_t)a.biases % 8 == 0
+                  ? 8 : 2;
+    if (Q4MV_MFMA_SB16 && sh.ks <= Q4MV_MFMA_SB16_MAX_KS && groups % 8 == 0 &&
+        (uintptr_t)a.scales % 16 == 0 && (uintptr_t)a.biases % 16 == 0 &&
+        lds0 + (size_t)sh.wpb * scratch_units(16) * 16 <= kMaxLds)
+        sbw = 16;
+    const size_t lds = lds0 + (size_t)sh.wpb * scratch_units(sbw) * 16;
     MfmaFn fn;
     if (sh.wpb == kMfmaWaves)
-        fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sb8)
-             : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sb8)
-             : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sb8)
-                          : pick<kMfmaWaves, 8>(nb16, sb8);
+        fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sbw)
+             : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sbw)
+             : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sbw)
+                          : pick<kMfmaWaves, 8>(nb16, sbw);
     else
-        fn = sh.ks == 1 ? pick<4, 1>(nb16, sb8) : sh.ks == 2 ? pick<4, 2>(nb16, sb8)
-                                                              : pick<4, 4>(nb16, sb8);
+        fn = sh.ks == 1 ? pick<4, 1>(nb16, sbw) : sh.ks == 2 ? pick<4, 2>(nb16, sbw)
+                                                              : pick<4, 4>(nb16, sbw);
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
     const int tpb = sh.wpb / sh.ks;
