@@ -69,10 +69,10 @@ inline size_t mfma_lds_bytes(int in_dim, int nb)
     return (size_t)nb * (4 * (in_dim / 32) + 1) * 16 + (size_t)(in_dim / 64) * 16 * 4;
 }
 // Partial-sum buffers of the MFMA kernel: 2 steps x tile groups per block x (ks - 1) parts
-// x 64 lanes x accumulators.
-inline size_t mfma_part_bytes(int wpb, int ks, bool nb16)
+// x lanes holding live rows x nacc accumulators.
+inline size_t mfma_part_bytes(int wpb, int ks, int nacc, int lanes)
 {
-    return (size_t)2 * (wpb / ks) * (ks - 1) * 64 * (nb16 ? 8 : 4) * 4;
+    return (size_t)2 * (wpb / ks) * (ks - 1) * lanes * nacc * 4;
 }
 // Launch shape of the MFMA kernel: waves per block and waves per tile (K-split); {0, 0} if
 // the shape's LDS does not fit in one compute unit.

@@ -66,6 +66,13 @@
 #ifndef Q4MV_MFMA_SB16_MAX_KS
 #define Q4MV_MFMA_SB16_MAX_KS 2
 #endif
+// Matrix-core shape: 16x16x32 (two 16-row output halves per 32-row tile; activation rows
+// 0..15 in one operand) for many tiles (at least KS4_BELOW) with K-split at most 2 and
+// nb outside 5..8, else 32x32x16 (activation rows padded to 32): each measured faster
+// (LM head NB 4 and 16 by about 2%; NB 8 and the short expert rows slower).
+#ifndef Q4MV_MFMA_MF16
+#define Q4MV_MFMA_MF16 1
+#endif
 #ifndef Q4MV_MFMA_BLOCKS_PER_CU
 #define Q4MV_MFMA_BLOCKS_PER_CU 4
 #endif
@@ -89,7 +96,7 @@ struct SbRegs { uint32_t v[4]; };
 // first unit of a part) and kept in the scratch for the next (groups % 8 == 0, 16-byte
 // aligned arrays; halves the scattered scale loads); 8 = one aligned 8-byte load per quad
 // (groups % 4 == 0, 8-byte aligned); 2 = four 2-byte loads with clamped indices.
-template <int WPB, int KS, bool NB16, int SBW>
+template <int WPB, int KS, bool NB16, int SBW, bool MF16>
 __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 {
     constexpr int TH = WPB * 64;
     constexpr int TPB = WPB / KS;  // tile groups per block
-    constexpr int NACC = NB16 ? 8 : 4;
+    constexpr int NACC = (MF16 || NB16) ? 8 : 4;
     extern __shared__ uint4 lds[];
     const int m = blockIdx.y;
     const int C = in_dim >> 5;
@@ -117,8 +124,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const int RS = 4 * C + 1;
     float4_t *const xsg_w = reinterpret_cast<float4_t *>(lds + nb * RS);
     float *const part = reinterpret_cast<float *>(xsg_w + groups * 4);
+    // lanes whose accumulators hold activation rows below nb (16x16x32: rows 4kb .. 4kb+3)
+    const int plan = MF16 ? 16 * ((nb + 3) >> 2) : 64;
     uint4 *const scratch_all =
-        reinterpret_cast<uint4 *>(part + (KS > 1 ? 2 * TPB * (KS - 1) * 64 * NACC : 0));
+        reinterpret_cast<uint4 *>(part + (KS > 1 ? 2 * TPB * (KS - 1) * plan * NACC : 0));
 
     // Stage activations and group sums. Called after each wave has issued its first weight
     // loads, so the two latencies overlap.
@@ -168,6 +177,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const int lane = threadIdx.x & 63;
     const int n = lane & 31;  // output row of the tile (B, D); activation row (A)
     const int h = lane >> 5;  // which chunk of the group this lane holds
+    // 16x16x32: lane (n16, kb) takes output row n16 of each 16-row half (B, D), activation
+    // row n16 (A), K slot kb: words 2kb and 2kb+1 of a group, one per MFMA; D rows
+    // 4kb .. 4kb+3
+    const int n16 = lane & 15, kb = lane >> 4;
     // wave index, made visibly wave-uniform so everything derived from it lives in SGPRs
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slot = wv / KS;     // tile group of this wave within the block
@@ -267,7 +280,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     };
 
     // this lane's activation row in LDS (row nb - 1 past nb), offset to its chunk parity
-    const uint4 *const xrow = lds + min(n, nb - 1) * RS + 4 * h;
+    const uint4 *const xrow =
+        MF16 ? lds + min(n16, nb - 1) * RS + 2 * kb : lds + min(n, nb - 1) * RS + 4 * h;
     float acc[NACC];
 
     // The block walks tile steps in lockstep when KS > 1 (one barrier per tile); with
@@ -309,70 +323,122 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 #pragma unroll
             for (int i = 0; i < NACC; i++) acc[i] = 0.0f;
         }
-        const uint2 s4 = SBW == 16 ? sbs[2 * n + (qx & 1)] : sbs[n];
-        const uint2 b4 = SBW == 16 ? sbs[2 * (32 + n) + (qx & 1)] : sbs[32 + n];
+        if constexpr (MF16) {
+            // scales and biases of this lane's two output rows (one per 16-row half)
+            uint2 s4[2], b4[2];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; g4++) {
-            const int g = 4 * qx + g4;
-            // uniform: the group lies in this wave's part and inside the row
-            const bool live = qd < q_end && g < groups;
-            const uint32_t sw = (g4 < 2) ? s4.x : s4.y, bw = (g4 < 2) ? b4.x : b4.y;
-            const uint32_t sbits = (g4 & 1) ? (sw & 0xFFFF0000u) : (sw << 16);
-            const uint32_t bbits = (g4 & 1) ? (bw & 0xFFFF0000u) : (bw << 16);
-            const float s = __uint_as_float(live ? sbits : 0u);
-            const float b = __uint_as_float(live ? bbits : 0u);
-            const uint4 bc = scratch[n * 8 + ((2 * g4 + h) ^ (n & 7))];
-            const int gx = min(g, groups - 1);
-            const uint4 *xg = xrow + 8 * gx;
-            const uint32_t wd[4] = {bc.x, bc.y, bc.z, bc.w};
-            float16_t d;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint32_t w8 = wd[j] >> 8;
-                const uint4 bq = {wd[j] & 0x000F000Fu, wd[j] & 0x00F000F0u, w8 & 0x000F000Fu,
-                                  w8 & 0x00F000F0u};
-                const half8_t aj = __builtin_bit_cast(half8_t, xg[j]);
-                d = __builtin_amdgcn_mfma_f32_32x32x16_f16(aj, __builtin_bit_cast(half8_t, bq),
-                                                           j == 0 ? float16_t{} : d, 0, 0, 0);
+            for (int t = 0; t < 2; t++) {
+                const int row = 16 * t + n16;
+                s4[t] = SBW == 16 ? sbs[2 * row + (qx & 1)] : sbs[row];
+                b4[t] = SBW == 16 ? sbs[2 * (32 + row) + (qx & 1)] : sbs[32 + row];
             }
-            // D layout: lane (n, h), register i holds activation row 8*(i/4) + 4h + i%4.
-            const float4_t xa4 = xsg[gx * 4 + h];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                acc[i] = __builtin_fmaf(s, d[i], __builtin_fmaf(b, xa4[i], acc[i]));
-            if constexpr (NB16) {
-                const float4_t xb4 = xsg[gx * 4 + 2 + h];
+            for (int g4 = 0; g4 < 4; g4++) {
+                const int g = 4 * qx + g4;
+                const bool live = qd < q_end && g < groups;
+                const int gx = min(g, groups - 1);
+                const uint4 *xg = xrow + 8 * gx;
+                const half8_t a0 = __builtin_bit_cast(half8_t, xg[0]);
+                const half8_t a1 = __builtin_bit_cast(half8_t, xg[1]);
+                // D layout: lane (n16, kb), register v holds activation row 4kb + v
+                const float4_t xa4 = xsg[gx * 4 + kb];
 #pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const int row = 16 * t + n16;
+                    // words 2kb, 2kb+1 of the group: chunk 2g4 + kb/2, bytes 8(kb%2) ..
+                    const uint2 bw = reinterpret_cast<const uint2 *>(
+                        scratch)[(row * 8 + ((2 * g4 + (kb >> 1)) ^ (row & 7))) * 2 + (kb & 1)];
+                    const uint32_t wd[2] = {bw.x, bw.y};
+                    float4_t d;
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        const uint32_t w8 = wd[j] >> 8;
+                        const uint4 bq = {wd[j] & 0x000F000Fu, wd[j] & 0x00F000F0u,
+                                          w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            j == 0 ? a0 : a1, __builtin_bit_cast(half8_t, bq),
+                            j == 0 ? float4_t{} : d, 0, 0, 0);
+                    }
+                    const uint32_t sw = (g4 < 2) ? s4[t].x : s4[t].y;
+                    const uint32_t bwd = (g4 < 2) ? b4[t].x : b4[t].y;
+                    const uint32_t sbits = (g4 & 1) ? (sw & 0xFFFF0000u) : (sw << 16);
+                    const uint32_t bbits = (g4 & 1) ? (bwd & 0xFFFF0000u) : (bwd << 16);
+                    const float s = __uint_as_float(live ? sbits : 0u);
+                    const float b = __uint_as_float(live ? bbits : 0u);
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        acc[4 * t + v] =
+                            __builtin_fmaf(s, d[v], __builtin_fmaf(b, xa4[v], acc[4 * t + v]));
+                }
+            }
+        } else {
+            const uint2 s4 = SBW == 16 ? sbs[2 * n + (qx & 1)] : sbs[n];
+            const uint2 b4 = SBW == 16 ? sbs[2 * (32 + n) + (qx & 1)] : sbs[32 + n];
+    #pragma unroll
+            for (int g4 = 0; g4 < 4; g4++) {
+                const int g = 4 * qx + g4;
+                // uniform: the group lies in this wave's part and inside the row
+                const bool live = qd < q_end && g < groups;
+                const uint32_t sw = (g4 < 2) ? s4.x : s4.y, bw = (g4 < 2) ? b4.x : b4.y;
+                const uint32_t sbits = (g4 & 1) ? (sw & 0xFFFF0000u) : (sw << 16);
+                const uint32_t bbits = (g4 & 1) ? (bw & 0xFFFF0000u) : (bw << 16);
+                const float s = __uint_as_float(live ? sbits : 0u);
+                const float b = __uint_as_float(live ? bbits : 0u);
+                const uint4 bc = scratch[n * 8 + ((2 * g4 + h) ^ (n & 7))];
+                const int gx = min(g, groups - 1);
+                const uint4 *xg = xrow + 8 * gx;
+                const uint32_t wd[4] = {bc.x, bc.y, bc.z, bc.w};
+                float16_t d;
+    #pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t w8 = wd[j] >> 8;
+                    const uint4 bq = {wd[j] & 0x000F000Fu, wd[j] & 0x00F000F0u, w8 & 0x000F000Fu,
+                                      w8 & 0x00F000F0u};
+                    const half8_t aj = __builtin_bit_cast(half8_t, xg[j]);
+                    d = __builtin_amdgcn_mfma_f32_32x32x16_f16(aj, __builtin_bit_cast(half8_t, bq),
+                                                               j == 0 ? float16_t{} : d, 0, 0, 0);
+                }
+                // D layout: lane (n, h), register i holds activation row 8*(i/4) + 4h + i%4.
+                const float4_t xa4 = xsg[gx * 4 + h];
+    #pragma unroll
                 for (int i = 0; i < 4; i++)
-                    acc[4 + i] = __builtin_fmaf(s, d[4 + i], __builtin_fmaf(b, xb4[i], acc[4 + i]));
+                    acc[i] = __builtin_fmaf(s, d[i], __builtin_fmaf(b, xa4[i], acc[i]));
+                if constexpr (NB16) {
+                    const float4_t xb4 = xsg[gx * 4 + 2 + h];
+    #pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        acc[4 + i] = __builtin_fmaf(s, d[4 + i], __builtin_fmaf(b, xb4[i], acc[4 + i]));
+                }
             }
         }
         if (last) {
             // combine the parts in LDS: parts 1..KS-1 publish, part 0 adds them in order
             if constexpr (KS > 1) {
-                float *pbuf = part + (size_t)(((step & 1) * TPB + slot) * (KS - 1)) * 64 * NACC;
-                if (quarter > 0) {
+                float *pbuf =
+                    part + (size_t)(((step & 1) * TPB + slot) * (KS - 1)) * plan * NACC;
+                if (quarter > 0 && lane < plan) {
 #pragma unroll
                     for (int i = 0; i < NACC; i++)
-                        pbuf[((quarter - 1) * NACC + i) * 64 + lane] = acc[i];
+                        pbuf[((quarter - 1) * NACC + i) * plan + lane] = acc[i];
                 }
                 __syncthreads();
-                if (quarter == 0) {
+                if (quarter == 0 && lane < plan) {
 #pragma unroll
                     for (int qq = 0; qq < KS - 1; qq++)
 #pragma unroll
-                        for (int i = 0; i < NACC; i++) acc[i] += pbuf[(qq * NACC + i) * 64 + lane];
+                        for (int i = 0; i < NACC; i++)
+                            acc[i] += pbuf[(qq * NACC + i) * plan + lane];
                 }
             }
             if (quarter == 0) {
-                const int orow = tile_row(tile) + n;
-                if (tile < tiles && orow < out_dim) {
 #pragma unroll
-                    for (int i = 0; i < NACC; i++) {
-                        const int r = 8 * (i / 4) + 4 * h + (i % 4);
-                        if (r < nb)
-                            y_m[(size_t)r * out_dim + orow] = gemv_epilogue(acc[i] * kTwo24, epi_div);
-                    }
+                for (int i = 0; i < NACC; i++) {
+                    // 16x16x32: half i/4, activation row 4kb + i%4; 32x32x16: activation
+                    // row 8(i/4) + 4h + i%4
+                    const int orow = tile_row(tile) + (MF16 ? 16 * (i / 4) + n16 : n);
+                    const int r = MF16 ? 4 * kb + (i % 4) : 8 * (i / 4) + 4 * h + (i % 4);
+                    if (tile < tiles && orow < out_dim && r < nb)
+                        y_m[(size_t)r * out_dim + orow] = gemv_epilogue(acc[i] * kTwo24, epi_div);
                 }
             }
             step++;
@@ -388,18 +454,34 @@ typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const 
                        const uint2 *, const float *, float *, int, int, int, float,
                        const int *, int, int);
 
-template <int WPB, int KS, bool NB16>
+static bool use_mf16(int ks, int nb, long tiles)
+{
+    return Q4MV_MFMA_MF16 && ks <= 2 && tiles >= Q4MV_MFMA_KS4_BELOW && (nb <= 4 || nb > 8);
+}
+
+template <int WPB, int KS, bool NB16, bool MF16>
 static MfmaFn pick_sb(int sbw)
 {
-    return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16>
-           : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8>
-                      : mfma_kernel<WPB, KS, NB16, 2>;
+    return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16, MF16>
+           : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8, MF16>
+                      : mfma_kernel<WPB, KS, NB16, 2, MF16>;
 }
 
 template <int WPB, int KS>
-static MfmaFn pick(bool nb16, int sbw)
+static MfmaFn pick(bool nb16, int sbw, bool mf16)
 {
-    return nb16 ? pick_sb<WPB, KS, true>(sbw) : pick_sb<WPB, KS, false>(sbw);
+    // the 16x16x32 path covers 16 activation rows either way
+    if constexpr (KS <= 2)
+        if (mf16) return pick_sb<WPB, KS, false, true>(sbw);
+    return nb16 ? pick_sb<WPB, KS, true, false>(sbw) : pick_sb<WPB, KS, false, false>(sbw);
+}
+
+// Partial-sum bytes of a launch shape: accumulators per lane, and the lanes that hold
+// activation rows below nb (the ones that publish).
+static size_t part_bytes(int wpb, int ks, int nb, long tiles)
+{
+    return use_mf16(ks, nb, tiles) ? mfma_part_bytes(wpb, ks, 8, 16 * ((nb + 3) / 4))
+                                   : mfma_part_bytes(wpb, ks, nb > 8 ? 8 : 4, 64);
 }
 
 static int mfma_ks(long tiles, int quads)
@@ -411,14 +493,13 @@ static int mfma_ks(long tiles, int quads)
 
 MfmaShape mfma_shape(int in_dim, int nb, long tiles)
 {
-    const bool nb16 = nb > 8;
     const int quads = (in_dim / 64 + 3) / 4;
     // 8 waves per block when the activations, the per-wave scratch and the partial sums fit
     // in LDS (with a smaller K-split if need be), else 4 waves
     for (int wpb = kMfmaWaves; wpb >= 4; wpb >>= 1) {
         const size_t base = mfma_lds_bytes(in_dim, nb) + (size_t)wpb * kScratchUnits * 16;
         for (int ks = std::min(mfma_ks(tiles, quads), wpb); ks >= 1; ks >>= 1)
-            if (base + mfma_part_bytes(wpb, ks, nb16) <= kMaxLds) return {wpb, ks};
+            if (base + part_bytes(wpb, ks, nb, tiles) <= kMaxLds) return {wpb, ks};
     }
     return {0, 0};
 }
@@ -430,7 +511,9 @@ hipError_t launch_mfma(const GemvArgs &a)
     const long tiles = (a.out_dim + 31) / 32;
     const MfmaShape sh = mfma_shape(a.in_dim, a.nb, tiles * a.n_mat);
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
-    const size_t lds0 = mfma_lds_bytes(a.in_dim, a.nb) + mfma_part_bytes(sh.wpb, sh.ks, nb16);
+    const bool mf16 = use_mf16(sh.ks, a.nb, tiles * a.n_mat);
+    const size_t lds0 =
+        mfma_lds_bytes(a.in_dim, a.nb) + part_bytes(sh.wpb, sh.ks, a.nb, tiles * a.n_mat);
     // 16-byte scale loads when the layout allows and their larger scratch still fits
     int sbw = groups % 4 == 0 && (uintptr_t)a.scales % 8 == 0 && (uintptr_t)a.biases % 8 == 0
                   ? 8 : 2;
@@ -441,13 +524,13 @@ hipError_t launch_mfma(const GemvArgs &a)
     const size_t lds = lds0 + (size_t)sh.wpb * scratch_units(sbw) * 16;
     MfmaFn fn;
     if (sh.wpb == kMfmaWaves)
-        fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sbw)
-             : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sbw)
-             : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sbw)
-                          : pick<kMfmaWaves, 8>(nb16, sbw);
+        fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sbw, mf16)
+             : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sbw, mf16)
+             : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sbw, mf16)
+                          : pick<kMfmaWaves, 8>(nb16, sbw, mf16);
     else
-        fn = sh.ks == 1 ? pick<4, 1>(nb16, sbw) : sh.ks == 2 ? pick<4, 2>(nb16, sbw)
-                                                              : pick<4, 4>(nb16, sbw);
+        fn = sh.ks == 1 ? pick<4, 1>(nb16, sbw, mf16) : sh.ks == 2 ? pick<4, 2>(nb16, sbw, mf16)
+                                                              : pick<4, 4>(nb16, sbw, mf16);
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
     const int tpb = sh.wpb / sh.ks;

@@ -110,3 +110,20 @@ def test_ragged_shapes(oracle_lib, shape):
             assert err.value.status == -2
             continue
         parity(run(d, path).cpu().numpy(), y_ref, bound, f"{shape} path={path}")
+
+
+# many tiles (the MFMA kernel's 16x16x32 range: at least 1024 tiles, K-split <= 2, nb
+# outside 5..8) with ragged row counts, short and long rows, and the 32x32x16 range at nb 6
+LARGE = [(1, 40007, 512, 3), (1, 33001, 256, 12), (2, 17000, 1024, 16), (1, 36001, 640, 6),
+         (1, 32800, 2560, 1)]
+
+
+@pytest.mark.parametrize("shape", LARGE, ids=["x".join(map(str, s)) for s in LARGE])
+def test_mfma_many_tiles(oracle_lib, shape):
+    n_mat, out_dim, in_dim, nb = shape
+    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=sum(shape) + 1)
+    y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
+    d = upload(case)
+    for path in (q4.PATH_MFMA, q4.PATH_AUTO):
+        flush(f"[many tiles] {shape} path={path}")
+        parity(run(d, path).cpu().numpy(), y_ref, bound, f"{shape} path={path}")
