@@ -1,5 +1,6 @@
 // MFMA kernel of libq4mv: the affine-Q4 GEMV as a real contraction for larger activation
-// batches, on gfx950's v_mfma_f32_32x32x16_f16 (D[32][32] += A[32][16] * B[16][32]).
+// batches, on gfx950's v_mfma_f32_32x32x16_f16 (D[32][32] += A[32][16] * B[16][32]) or
+// v_mfma_f32_16x16x32_f16 (D[16][16] += A[16][32] * B[32][16]).
 //
 // Operands: A = activations (32 rows = activation rows; rows past nb are never stored), read
 // from LDS; B = codes of 32 output rows, unpacked in registers to f16 subnormals q*2^-24
@@ -14,7 +15,10 @@
 // subnormal, at most 2^-25 in x/16). The group's scale and bias are then applied in f32 (the
 // per-group fold of fn_q4_rows_h, Constant BATCH_MSL page, quantized_rows section). The
 // dequantised weight is never formed (the page's tiled expert GEMM dequantises to f16 tiles
-// instead).
+// instead). With 16x16x32 the tile is two 16-row halves: lane (n16, kb) (kb = lane / 16)
+// takes words 2kb and 2kb+1 of a group for row n16 of each half, one word per MFMA, and the
+// same two words' activations of activation row n16 (rows 0..15 fill the A operand, half
+// the A reads of the 32-row shape); two MFMAs per half and group.
 //
 // Loads: a wave's work unit is (tile, quad) = 32 rows x 4 scale groups (128 bytes of codes
 // per row). It is read from HBM as whole 128-byte lines (8 lanes per row, 8 rows per load
@@ -120,7 +124,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // word's B operand. RS = 4C + 1 (odd) puts 8 consecutive rows on 8 distinct bank quads.
     // Lanes of activation rows past nb read row nb - 1 instead: row m of D depends on row m
     // of A only, and rows past nb are never stored, so every A read is unconditional.
-    // Partial sums: part[2][TPB][KS-1][64][NACC] (double-buffered by tile step).
+    // Partial sums: part[2][TPB][KS-1][NACC][plan] (double-buffered by tile step; plan =
+    // the lanes that hold activation rows below nb).
     const int RS = 4 * C + 1;
     float4_t *const xsg_w = reinterpret_cast<float4_t *>(lds + nb * RS);
     float *const part = reinterpret_cast<float *>(xsg_w + groups * 4);
