@@ -76,6 +76,25 @@ constexpr bool kValuNT = Q4MV_VALU_NT != 0;
 #ifndef Q4MV_VALU_PAIR_ROWS
 #define Q4MV_VALU_PAIR_ROWS 2
 #endif
+// Scales and biases of a wave step: the step's rows are consecutive, so their scales (and
+// their biases) form one contiguous block; it is read with 16-byte loads (one instruction
+// for both arrays) into a per-wave LDS slot and each lane picks its values from there,
+// instead of one 2-byte load per lane, chunk and array.
+#ifndef Q4MV_VALU_SBLDS
+#define Q4MV_VALU_SBLDS 1
+#endif
+// ... used when every wave runs at least this many steps: the LDS round trip lengthens a
+// step's critical path, so short launches (a step or two per wave) are faster without it.
+#ifndef Q4MV_VALU_SBLDS_MIN_STEPS
+#define Q4MV_VALU_SBLDS_MIN_STEPS 4
+#endif
+
+// Per-wave LDS slot of the block-loaded scales and biases: 16-byte segments per array
+// (0 where the shape does not use it). A wave step's rows hold 32 * ROWS * CPL groups.
+constexpr int valu_sb_segs(int rows, int cpl, bool specialised)
+{
+    return Q4MV_VALU_SBLDS && specialised && rows * cpl <= 8 ? 4 * rows * cpl : 0;
+}
 
 // ---------------------------------------------------------------------------------------
 // Code widths. BITS = 4 is the affine-Q4 layout (one 16-byte chunk of 32 codes). BITS = 2 and
@@ -210,7 +229,7 @@ __device__ __forceinline__ float chunk_fold(uint32_t sbits, uint32_t bbits, floa
 
 // LOG2G, CPL > 0: lane-group size and chunks per lane fixed at compile time (the common row
 // lengths); LOG2G = -1, CPL = 0: both taken at run time (any in_dim).
-template <int NB, int ROWS, int LOG2G, int CPL, int BITS>
+template <int NB, int ROWS, int LOG2G, int CPL, int BITS, bool SBL = false>
 __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES) void valu_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
@@ -341,6 +360,18 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
         // ---- fully unrolled chunk loop
         uint4 cc[ROWS][CPL];
         uint32_t scb[ROWS][CPL], bcb[ROWS][CPL];
+        // block-loaded scales and biases (NSEG 16-byte segments per array): lanes 0..NSEG-1
+        // load the step's scale block, NSEG..2*NSEG-1 its bias block; both arrays must be
+        // 16-byte aligned (a step's block starts at a multiple of 64*ROWS*CPL bytes)
+        constexpr bool kPrefetch = BITS == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
+        constexpr int NSEG = (kPrefetch || kValuXDirect || !SBL) ? 0 : valu_sb_segs(ROWS, CPL, true);
+        const bool sbl = NSEG > 0 &&
+            ((reinterpret_cast<uintptr_t>(s_m) | reinterpret_cast<uintptr_t>(b_m)) & 15) == 0;
+        uint4 *const sbslot =
+            reinterpret_cast<uint4 *>(reinterpret_cast<char *>(lds) +
+                                      (((size_t)NB * C * 68 + 15) & ~(size_t)15)) +
+            (threadIdx.x >> 6) * 2 * NSEG;
+        uint4 sbv = {0u, 0u, 0u, 0u};
         // Loads are issued in the order compute() consumes them (chunk-major, then row), and
         // scales are converted where they are used, so the compiler's waits on the load
         // counter are progressive: a wave starts on its first chunk while the rest is still
@@ -356,12 +387,36 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
                 sr[t] = s_m + (size_t)row * groups;
                 br[t] = b_m + (size_t)row * groups;
             }
+            if (sbl) {
+                // segment L of the step's scale (L < NSEG) or bias block; the last step's
+                // block may end past out_dim: a segment that crosses the end of the array
+                // is read element by element up to it
+                if (lane < 2 * NSEG) {
+                    const bool isb = lane >= NSEG;
+                    const uint16_t *arr = isb ? b_m : s_m;
+                    const size_t e0 = (size_t)ws * rows_per_wave * groups + 8 * (lane - (isb ? NSEG : 0));
+                    const size_t lim = (size_t)out_dim * groups;
+                    if (e0 + 8 <= lim) {
+                        typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+                        const u32x4v v = __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4v *>(arr + e0));
+                        sbv = uint4{v[0], v[1], v[2], v[3]};
+                    } else {
+                        uint32_t h[8];
+#pragma unroll
+                        for (int i = 0; i < 8; i++) h[i] = e0 + i < lim ? arr[e0 + i] : 0u;
+                        sbv = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                    h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+                    }
+                }
+            }
 #pragma unroll
             for (int k = 0; k < CPL; k++) {
                 const int c = j + (k << log2g);
 #pragma unroll
                 for (int t = 0; t < ROWS; t++) {
                     cw[t][k] = load_chunk<BITS, kValuNT>(wr[t], c, C);
+                    if (sbl) continue;
 #if Q4MV_VALU_NT
                     // streamed once: non-temporal loads (no reuse to keep in the caches)
                     sv[t][k] = __builtin_nontemporal_load(sr[t] + (c >> 1));
@@ -374,6 +429,24 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
             }
         };
         auto compute = [&](int ws) {
+            if (sbl) {
+                // this step's blocks into the wave's slot, then each lane's values (LDS
+                // operations of one wave complete in order; the fences keep the compiler
+                // from moving them across each other)
+                asm volatile("" ::: "memory");
+                if (lane < 2 * NSEG) sbslot[lane] = sbv;
+                asm volatile("" ::: "memory");
+                const uint16_t *sl = reinterpret_cast<const uint16_t *>(sbslot);
+#pragma unroll
+                for (int t = 0; t < ROWS; t++)
+#pragma unroll
+                    for (int k = 0; k < CPL; k++) {
+                        const int el = (grp * ROWS + t) * groups + ((j + (k << log2g)) >> 1);
+                        scb[t][k] = sl[el];
+                        bcb[t][k] = sl[NSEG * 8 + el];
+                    }
+                asm volatile("" ::: "memory");
+            }
             float acc[ROWS][NB];
 #pragma unroll
             for (int t = 0; t < ROWS; t++)
@@ -570,11 +643,16 @@ static bool valu_specialised(int log2g, int cpl, int bits)
     return false;
 }
 
+// sbl: the block-loaded scale variant (one-row, nb = 1, Q4 only).
 template <int NB, int ROWS, int BITS>
-static ValuFn pick_shape(int log2g, int cpl)
+static ValuFn pick_shape(int log2g, int cpl, bool sbl = false)
 {
-#define Q4MV_PICK(L, K) \
-    if (log2g == L && cpl == K) return valu_kernel<NB, ROWS, L, K, BITS>;
+#define Q4MV_PICK(L, K)                                                                   \
+    if (log2g == L && cpl == K) {                                                         \
+        if constexpr (NB == 1 && ROWS == 1 && BITS == 4 && valu_sb_segs(1, K, true) > 0)  \
+            if (sbl) return valu_kernel<NB, ROWS, L, K, BITS, true>;                      \
+        return valu_kernel<NB, ROWS, L, K, BITS>;                                         \
+    }
     if constexpr (BITS == 4) {
         Q4MV_VALU_SHAPES(Q4MV_PICK)
     } else {
@@ -585,10 +663,10 @@ static ValuFn pick_shape(int log2g, int cpl)
 }
 
 template <int ROWS, int BITS>
-static ValuFn pick_nb(int nb, int log2g, int cpl)
+static ValuFn pick_nb(int nb, int log2g, int cpl, bool sbl)
 {
     switch (nb) {
-    case 1: return pick_shape<1, ROWS, BITS>(log2g, cpl);
+    case 1: return pick_shape<1, ROWS, BITS>(log2g, cpl, sbl);
     case 2: return pick_shape<2, ROWS, BITS>(log2g, cpl);
     case 3: return pick_shape<3, ROWS, BITS>(log2g, cpl);
     case 4: return pick_shape<4, ROWS, BITS>(log2g, cpl);
@@ -601,10 +679,10 @@ static ValuFn pick_nb(int nb, int log2g, int cpl)
 }
 
 template <int BITS>
-static ValuFn pick(int rows, int nb, int log2g, int cpl)
+static ValuFn pick(int rows, int nb, int log2g, int cpl, bool sbl)
 {
-    return rows == 1 ? pick_nb<1, BITS>(nb, log2g, cpl)
-                     : pick_nb<Q4MV_VALU_PAIR_ROWS, BITS>(nb, log2g, cpl);
+    return rows == 1 ? pick_nb<1, BITS>(nb, log2g, cpl, sbl)
+                     : pick_nb<Q4MV_VALU_PAIR_ROWS, BITS>(nb, log2g, cpl, false);
 }
 
 static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
@@ -613,19 +691,28 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     const int C = a.in_dim / 32;
     const int cpl = C >> log2g;
     if (rows == 2) rows = Q4MV_VALU_PAIR_ROWS;
-    ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl)
-                : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl)
-                              : pick<4>(rows, nbp, log2g, cpl);
+    const int rows_per_wave = (64 >> log2g) * rows;
+    const long wave_steps = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
+    const long blocks_needed = (wave_steps + 3) / 4;
+    // block-loaded scales (one-row kernel, nb = 1, Q4) when the waves of two blocks per CU
+    // would each run several steps
+    const bool prefetch = a.bits == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
+    const int nseg =
+        kValuXDirect || prefetch || rows != 1 || nbp != 1 || a.bits != 4 ||
+                wave_steps * a.n_mat < (long)Q4MV_VALU_SBLDS_MIN_STEPS * device_cus() * 2 * 4
+            ? 0 : valu_sb_segs(rows, cpl, valu_specialised(log2g, cpl, a.bits));
+    ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl, false)
+                : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl, false)
+                              : pick<4>(rows, nbp, log2g, cpl, nseg > 0);
     // activations straight into registers need no LDS (same rule as the kernel's XREG; the
     // generic kernel and NB > 4 always stage)
     const bool xdirect = kValuXDirect && nbp <= 4 && valu_specialised(log2g, cpl, a.bits) &&
                          nbp * cpl <= Q4MV_VALU_XREG_MAX;
-    const size_t lds = xdirect ? 0 : (size_t)nbp * C * 64 + (size_t)nbp * C * 4;
+    const size_t lds = xdirect ? 0
+                               : (((size_t)nbp * C * 68 + 15) & ~(size_t)15) +
+                                     (size_t)(kValuThreads / 64) * 2 * nseg * 16;
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
-    const int rows_per_wave = (64 >> log2g) * rows;
-    const long wave_steps = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
-    const long blocks_needed = (wave_steps + 3) / 4;
     // persistent blocks: enough to fill every CU a few times over, shared by the matrices
     const long per_cu = std::min<long>(rows != 1      ? Q4MV_VALU_BLOCKS_PER_CU
                                        : a.bits == 4 ? Q4MV_VALU1_BLOCKS_PER_CU

@@ -127,3 +127,32 @@ def test_mfma_many_tiles(oracle_lib, shape):
     for path in (q4.PATH_MFMA, q4.PATH_AUTO):
         flush(f"[many tiles] {shape} path={path}")
         parity(run(d, path).cpu().numpy(), y_ref, bound, f"{shape} path={path}")
+
+
+# Long one-row launches at nb = 1 (every wave runs several row steps): the kernel reads a
+# step's scales and biases as two contiguous blocks. Ragged row counts make the last step's
+# block end inside a 16-byte segment (read element by element up to the array's end).
+BLOCK_SCALES = [(1, 40003, 2560, 1), (1, 65537, 512, 1), (1, 16385, 2048, 1)]
+
+
+@pytest.mark.parametrize("shape", BLOCK_SCALES, ids=["x".join(map(str, s)) for s in BLOCK_SCALES])
+def test_block_loaded_scales(oracle_lib, shape):
+    n_mat, out_dim, in_dim, nb = shape
+    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=sum(shape) + 2)
+    y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
+    d = upload(case)
+    flush(f"[block scales] {shape}")
+    y1 = run(d, q4.PATH_VALU)
+    parity(y1.cpu().numpy(), y_ref, bound, f"{shape} one-row")
+    # the same values through the per-chunk scale loads: the two-row kernel (bitwise the
+    # one-row result) and scale/bias arrays that are only 8-byte aligned
+    if out_dim % 2 == 0:
+        assert torch.equal(run(d, q4.PATH_VALU_2ROW), y1)
+    for name in ("s", "b"):
+        t = d[name]
+        buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+        d[name] = buf[4:4 + t.numel()].view(t.shape)
+        d[name].copy_(t)
+        assert d[name].data_ptr() % 16 == 8
+    flush(f"[block scales] {shape} 8-byte aligned scales")
+    assert torch.equal(run(d, q4.PATH_VALU), y1)
