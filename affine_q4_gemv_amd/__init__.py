@@ -53,6 +53,7 @@ def lib():
         L.q4mv.argtypes = gemv + [p]
         L.q4mv_2row.argtypes = gemv + [p]
         L.q4mv_path.argtypes = gemv + [i32, p]
+        L.q4mv_fused.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, p]
         L.q4mv_silu.argtypes = gemv + [f32, p]
         L.q4mv_path_silu.argtypes = gemv + [f32, i32, p]
         L.q4mv_swiglu_prep.argtypes = [p, i32, i32, p, p, p, p]
@@ -66,6 +67,7 @@ def lib():
         L.q4mv_status_str.restype = ctypes.c_char_p
         L.q4mv_version.argtypes = []
         for fn in ("q4mv_pack_codes", "q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_path",
+                   "q4mv_fused",
                    "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_quantize",
                    "q4mv_auto_path",
                    "q4mv_version"):
@@ -182,6 +184,27 @@ def q4mv_2row(w, scales, biases, xe, xo, xsum, nb, y=None, stream=None):
 def q4mv_path(w, scales, biases, xe, xo, xsum, nb, path, y=None, stream=None):
     """:func:`q4mv` with an explicit kernel (PATH_VALU, PATH_VALU_2ROW, PATH_MFMA)."""
     return _gemv("q4mv_path", w, scales, biases, xe, xo, xsum, nb, y, stream, path=path)
+
+
+def q4mv_fused(w, scales, biases, x, nb, path=PATH_AUTO, y=None, stream=None):
+    """:func:`q4mv_prepare_x` + :func:`q4mv_path` in one launch from f32 activations
+    x [n_mat*nb, in_dim]; bitwise the two-call result on the same path."""
+    torch = _torch()
+    if w.dim() != 3:
+        raise ValueError("w: expected [n_mat, out_dim, in_dim/8]")
+    n_mat, out_dim, w8 = w.shape
+    in_dim = w8 * 8
+    _need(w, torch.int32, (n_mat, out_dim, w8), "w")
+    _need(scales, torch.bfloat16, (n_mat, out_dim, in_dim // 64), "scales")
+    _need(biases, torch.bfloat16, (n_mat, out_dim, in_dim // 64), "biases")
+    _need(x, torch.float32, (n_mat * nb, in_dim), "x")
+    if y is None:
+        y = torch.empty((n_mat, nb, out_dim), dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, (n_mat, nb, out_dim), "y")
+    _check("q4mv_fused", lib().q4mv_fused(w.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                           x.data_ptr(), y.data_ptr(), n_mat, out_dim, in_dim,
+                                           nb, int(path), _stream(w, stream)))
+    return y
 
 
 def q4mv_silu(w, scales, biases, xe, xo, xsum, nb, div, y=None, stream=None):

@@ -155,6 +155,27 @@ int q4mv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, cons
                     auto_path(in_dim, nb, false, out_dim), stream);
 }
 
+int q4mv_fused(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+               const float *x, float *y, int n_mat, int out_dim, int in_dim, int nb, int path,
+               void *stream)
+{
+    if (!x) return Q4MV_ERR_NULL;
+    // xe, xo, xsum are not read: stand-ins that pass the shared checks
+    int st = check_gemv(w, scales, biases, w, w, y, y, n_mat, out_dim, in_dim, nb);
+    if (st != Q4MV_OK) return st;
+    if (!aligned(x, 16)) return Q4MV_ERR_ALIGN;
+    if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
+    if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
+    if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
+    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_mat * ((out_dim + 31) / 32)).wpb == 0)
+        return Q4MV_ERR_SHAPE;
+    GemvArgs a{w, scales, biases, nullptr, nullptr, nullptr, y, n_mat, out_dim, in_dim, nb,
+               0.0f, static_cast<hipStream_t>(stream)};
+    a.xf = x;
+    hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
 int q4mv_silu(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
               int out_dim, int in_dim, int nb, float div, void *stream)

@@ -25,6 +25,9 @@ struct GemvArgs {
     int x_shared = 0;
     // Code width: 4 (affine-Q4), or the low-bit layouts 2 and 3 (VALU kernels only).
     int bits = 4;
+    // f32 activations [rows][in_dim] (rows as for xe): the kernels stage them with the prep
+    // done in the block (xe, xo and xsum are then not read).
+    const float *xf = nullptr;
 };
 
 // Kernel paths (same numbering as q4mv_path in q4mv.h).

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
     int out_dim, int in_dim, int nb, float epi_div, const int *__restrict__ sel,
-    int n_bank, int x_shared)
+    int n_bank, int x_shared, const float *__restrict__ xf)
 {
     constexpr int TH = WPB * 64;
     constexpr int TPB = WPB / KS;  // tile groups per block
@@ -136,7 +136,64 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 
     // Stage activations and group sums. Called after each wave has issued its first weight
     // loads, so the two latencies overlap.
+    // Fused prep (xf non-null: f32 activations): the f16 rounding, the 1/16 of the odd
+    // pair members and the chunk sums of q4mv_prepare_x done here with the same additions
+    // (pair sums, a balanced tree over a chunk's 16 pairs: each thread adds its word's four
+    // pairs, two quad DPP steps add the chunk's four words; then a group's two chunks in
+    // order), so the LDS contents are bitwise those staged from q4mv_prepare_x's outputs.
+    // One thread per 8-column word; a quad of lanes is one chunk, 8 lanes one group (words
+    // per row are a multiple of 8).
+    auto fstage = [&]() {
+        const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
+        const float4 *xf_m = reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)(in_dim >> 2);
+        const int wrow = in_dim >> 3, words = nb * wrow;
+        float *xsw = reinterpret_cast<float *>(xsg_w);
+        const _Float16 sixteenth = (_Float16)0.0625f;
+        for (int base = threadIdx.x; base < words; base += 2 * TH) {
+            float4 v[2][2];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int wi = min(base + i * TH, words - 1);
+                v[i][0] = xf_m[2 * wi];
+                v[i][1] = xf_m[2 * wi + 1];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int wi = base + i * TH;
+                if (wi < words) {  // uniform per 8 lanes
+                    const int r = wi / wrow, kw = wi - r * wrow;
+                    const float f[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w,
+                                        v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
+                    _Float16 h[8];
+#pragma unroll
+                    for (int t = 0; t < 8; t++) h[t] = (_Float16)f[t];
+                    float ps[4];
+#pragma unroll
+                    for (int q = 0; q < 4; q++) ps[q] = (float)h[2 * q] + (float)h[2 * q + 1];
+                    float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                    sum += dpp<0xB1>(sum);
+                    sum += dpp<0x4E>(sum);
+                    const float other = __shfl_xor(sum, 4, 64);  // the group's other chunk
+                    if ((kw & 7) == 0) xsw[(kw >> 3) * 16 + r] = (sum + other) * kTwoM24;
+                    // unit r*RS + 4c + j: (x0, x4) (x1/16, x5/16) (x2, x6) (x3/16, x7/16)
+                    uint4 u;
+                    u.x = __builtin_bit_cast(uint32_t, half2_t{h[0], h[4]});
+                    u.y = __builtin_bit_cast(uint32_t, half2_t{h[1] * sixteenth, h[5] * sixteenth});
+                    u.z = __builtin_bit_cast(uint32_t, half2_t{h[2], h[6]});
+                    u.w = __builtin_bit_cast(uint32_t, half2_t{h[3] * sixteenth, h[7] * sixteenth});
+                    lds[r * RS + kw] = u;
+                }
+            }
+        }
+        for (int u = threadIdx.x; u < groups * 16; u += TH)
+            if ((u & 15) >= nb) xsw[u] = 0.0f;
+        __syncthreads();
+    };
     auto stage = [&]() {
+        if (xf) {
+            fstage();
+            return;
+        }
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
         const uint2 *xe_m = xe + xrow0 * words8;
         const uint2 *xo_m = xo + xrow0 * words8;
@@ -457,7 +514,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 
 typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, float,
-                       const int *, int, int);
+                       const int *, int, int, const float *);
 
 static bool use_mf16(int ks, int nb, long tiles)
 {
@@ -554,7 +611,8 @@ hipError_t launch_mfma(const GemvArgs &a)
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(sh.wpb * 64), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
-                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, a.epi_div, a.sel, a.n_bank, a.x_shared);
+                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, a.epi_div, a.sel, a.n_bank, a.x_shared,
+                       a.xf);
     return hipGetLastError();
 }
 

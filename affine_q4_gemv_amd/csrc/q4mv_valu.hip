@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
     int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt, float epi_div,
-    const int *__restrict__ sel, int n_bank, int x_shared)
+    const int *__restrict__ sel, int n_bank, int x_shared, const float *__restrict__ xf)
 {
     const int log2g = LOG2G >= 0 ? LOG2G : log2g_rt;
     extern __shared__ uint4 lds[];
@@ -289,7 +289,68 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
         }
         __syncthreads();
     };
+    // Fused prep (xf non-null: f32 activations): the block rounds its rows to f16 itself
+    // and forms each 32-column chunk's sum of the rounded values with the additions of
+    // q4mv_prepare_x (pair sums, then a balanced tree over the chunk's 16 pairs: each thread
+    // adds its word's four pairs, two quad DPP steps add the chunk's four words), so the
+    // staged LDS contents are bitwise those staged from q4mv_prepare_x's outputs. One thread
+    // per 8-column word; a quad of lanes is one chunk (words per row are a multiple of 8).
+    const int words = NB * (in_dim >> 3);
+    const float4 *xf_m = xf ? reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)(in_dim >> 2)
+                            : nullptr;
+    struct FStage { float4 v[2][2]; };
+    auto fstage_load = [&](int base, FStage &st) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int wi = min(base + i * kValuThreads, words - 1);
+            st.v[i][0] = xf_m[2 * wi];
+            st.v[i][1] = xf_m[2 * wi + 1];
+        }
+    };
+    auto fstage_store = [&](int base, const FStage &st) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int wi = base + i * kValuThreads;
+            if (wi < words) {  // uniform per quad
+                const int r = wi / (in_dim >> 3), kw = wi - r * (in_dim >> 3);
+                const float f[8] = {st.v[i][0].x, st.v[i][0].y, st.v[i][0].z, st.v[i][0].w,
+                                    st.v[i][1].x, st.v[i][1].y, st.v[i][1].z, st.v[i][1].w};
+                _Float16 h[8];
+#pragma unroll
+                for (int t = 0; t < 8; t++) h[t] = (_Float16)f[t];
+                float ps[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) ps[q] = (float)h[2 * q] + (float)h[2 * q + 1];
+                float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                sum += dpp<0xB1>(sum);
+                sum += dpp<0x4E>(sum);
+                if ((kw & 3) == 0) xsw[r * C + (kw >> 2)] = sum * kTwoM24;
+                // pair layout: (x0, x4) (x1, x5) (x2, x6) (x3, x7)
+                uint4 u;
+                u.x = __builtin_bit_cast(uint32_t, half2_t{h[0], h[4]});
+                u.y = __builtin_bit_cast(uint32_t, half2_t{h[1], h[5]});
+                u.z = __builtin_bit_cast(uint32_t, half2_t{h[2], h[6]});
+                u.w = __builtin_bit_cast(uint32_t, half2_t{h[3], h[7]});
+                lds[x_unit(r, kw >> 2, kw & 3, C)] = u;
+            }
+        }
+    };
+    auto fstage_finish = [&](const FStage &st0) {
+        fstage_store(threadIdx.x, st0);
+        for (int base = threadIdx.x + 2 * kValuThreads; base < words; base += 2 * kValuThreads) {
+            FStage st;
+            fstage_load(base, st);
+            fstage_store(base, st);
+        }
+        __syncthreads();
+    };
     auto stage = [&]() {
+        if (xf) {
+            FStage st0;
+            fstage_load(threadIdx.x, st0);
+            fstage_finish(st0);
+            return;
+        }
         XStage st0;
         stage_load(threadIdx.x, st0);
         stage_finish(st0);
@@ -532,10 +593,17 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
 #if Q4MV_VALU_XFIRST
             // activations first (small, mostly cache hits), then the first step's weights:
             // the staging only waits for its own loads
-            XStage st0;
-            stage_load(threadIdx.x, st0);
-            if (ws < wave_steps) load(ws, cc, scb, bcb);
-            stage_finish(st0);
+            if (xf) {
+                FStage st0;
+                fstage_load(threadIdx.x, st0);
+                if (ws < wave_steps) load(ws, cc, scb, bcb);
+                fstage_finish(st0);
+            } else {
+                XStage st0;
+                stage_load(threadIdx.x, st0);
+                if (ws < wave_steps) load(ws, cc, scb, bcb);
+                stage_finish(st0);
+            }
 #else
             if (ws < wave_steps) load(ws, cc, scb, bcb);  // first step's weights, before staging
             stage();
@@ -616,7 +684,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
 
 typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, int, int, int,
-                       float, const int *, int, int);
+                       float, const int *, int, int, const float *);
 
 // (log2 G, CPL) of the specialised row lengths: in_dim = 32 * CPL << log2G.
 #define Q4MV_VALU_SHAPES(X)                                                                   \
@@ -731,7 +799,7 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
                        a.xsum, a.y, a.out_dim, a.in_dim, a.nb, r0, log2g, cpl, a.epi_div,
-                       a.sel, a.n_bank, a.x_shared);
+                       a.sel, a.n_bank, a.x_shared, a.xf);
     return hipGetLastError();
 }
 

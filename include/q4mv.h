@@ -133,7 +133,7 @@ int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
  * q4mv_path -- q4mv with an explicit kernel choice instead of the nb-based dispatch.
  *   path 0: automatic (what q4mv does), 1: VALU dot-product kernel, one row per lane group,
  *   2: VALU kernel, two rows per lane group (q4mv_2row; out_dim must be even),
- *   3: MFMA kernel (32x32x16 f16 matrix cores; activation rows padded to 32).
+ *   3: MFMA kernel (16x16x32 or 32x32x16 f16 matrix cores).
  * Same arguments, layouts and errors as q4mv, plus PATH for an unknown path, and SHAPE when
  * path 3 is asked for a shape whose staged activations and sums
  * (nb*(in_dim/8+1)*16 + in_dim bytes) plus an 18 KB scratch do not fit in the 160 KB of LDS
@@ -144,6 +144,22 @@ int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
 int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
               int out_dim, int in_dim, int nb, int path, void *stream);
+
+/*
+ * q4mv_fused -- q4mv_prepare_x and q4mv in one launch: the GEMV takes the f32 activations
+ * and each workgroup does the prep of its rows while it stages them (f16 rounding of every
+ * value, and per 32-column chunk the f32 sum of the rounded values with the same additions
+ * in the same order as q4mv_prepare_x). The activation prep of fn_norm_prep_b /
+ * fn_moe_act_b (Constant BATCH_MSL page) is thus folded into the product instead of being a
+ * launch of its own, and no xe/xo/xsum buffers are needed.
+ *   x     : f32 [n_mat*nb][in_dim], 16-byte aligned; matrix m reads rows m*nb .. m*nb+nb-1
+ *   path  : as q4mv_path (0 = the automatic dispatch of q4mv)
+ * Other arguments, layouts and errors as q4mv_path. The result is bitwise what
+ * q4mv_prepare_x followed by q4mv_path gives on the same path.
+ */
+int q4mv_fused(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+               const float *x, float *y, int n_mat, int out_dim, int in_dim, int nb, int path,
+               void *stream);
 
 /*
  * q4mv_silu -- q4mv with the output passed through silu(y / div):

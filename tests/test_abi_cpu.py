@@ -30,7 +30,7 @@ def test_header_declares_expected_entry_points():
     for name in ("q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_pack_codes", "q4mv_path",
                  "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_auto_path",
                  "q4mv_quantize", "q4mv_experts", "q4mv_combine", "q4mv_pack_lowbit",
-                 "q4mv_lowbit",
+                 "q4mv_lowbit", "q4mv_fused",
                  "q4mv_status_str", "q4mv_version"):
         assert name in fns
 
@@ -218,3 +218,21 @@ def test_lowbit_validation(L):
     assert g(3, A, A, 1 << 26, 2048, None) == ESHAPE
     assert g(2, A + 8, A, 1, 64, None) == EALIGN
     assert g(3, A, A + 2, 1, 64, None) == EALIGN
+
+
+def test_fused_validation(L):
+    """q4mv_fused: f32 x instead of the prep buffers; the other checks as q4mv_path."""
+    def args(**kw):
+        a = dict(w=A, s=A, b=A, x=A, y=A, n_mat=1, out=8, ind=128, nb=1, path=0)
+        a.update(kw)
+        return [a["w"], a["s"], a["b"], a["x"], a["y"], a["n_mat"], a["out"], a["ind"],
+                a["nb"], a["path"], None]
+    for k in ("w", "s", "b", "x", "y"):
+        assert L.q4mv_fused(*args(**{k: None})) == ENULL
+    for kw in (dict(n_mat=0), dict(out=0), dict(ind=96), dict(nb=0), dict(nb=17),
+               dict(nb=16, ind=4160)):
+        assert L.q4mv_fused(*args(**kw)) == ESHAPE, kw
+    for kw in (dict(w=A + 4), dict(x=A + 8), dict(s=A + 1), dict(y=A + 2)):
+        assert L.q4mv_fused(*args(**kw)) == EALIGN, kw
+    assert L.q4mv_fused(*args(path=4)) == EPATH
+    assert L.q4mv_fused(*args(out=7, path=2)) == EODD
