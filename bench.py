@@ -1,7 +1,9 @@
 """Benchmark of the affine-Q4 GEMV hot path on one MI355X.
 
-One step = q4mv_prepare_x (activation prep) + q4mv (the GEMV) over one batch of synthetic
-inputs already resident in HBM. Weights rotate over R copies whose total exceeds twice the
+One step = q4mv_fused over one batch of synthetic inputs already resident in HBM: the GEMV
+with the activation prep (f16 rounding, per-chunk sums) done inside its own staging, one
+launch, bitwise what q4mv_prepare_x followed by q4mv gives (checked in the run); the
+two-launch step is reported next to it in the sweep. Weights rotate over R copies whose total exceeds twice the
 256 MB Infinity Cache, so every launch streams its weights from HBM. Timed loops are captured
 in a HIP graph (replayed after a warm-up replay), so host launch cost is not measured; a
 replay's output is checked bit for bit against an eager call.
@@ -69,7 +71,7 @@ def load_traffic(workload, nb, kernel):
 class Problem:
     """Device buffers of one workload: R rotated weight copies, activations and outputs."""
 
-    def __init__(self, name, nb, rotate=True, silu_div=None, bits=4):
+    def __init__(self, name, nb, rotate=True, silu_div=None, bits=4, fused=False):
         import numpy as np
         import torch
 
@@ -79,6 +81,7 @@ class Problem:
         self.q4, self.torch = q4, torch
         self.silu_div = silu_div
         self.bits = bits
+        self.fused = fused and bits == 4 and silu_div is None
         c = workloads.make_case(name, nb=nb)
         self.name = name
         self.n_mat, self.out_dim, self.in_dim, self.nb = c["n_mat"], c["out_dim"], c["in_dim"], nb
@@ -103,28 +106,32 @@ class Problem:
         self.xe, self.xo, self.xsum = q4.q4mv_prepare_x(self.x)
         self.y = torch.empty((self.n_mat, nb, self.out_dim), dtype=torch.float32, device=dev)
         rows = self.n_mat * nb
-        self.algo_bytes = self.algorithmic_bytes(name, nb)
+        self.algo_bytes = self.algorithmic_bytes(name, nb, self.fused)
         self.path = q4.q4mv_auto_path(self.in_dim, nb, False, self.out_dim)
         self.kernel = "mfma_kernel" if self.path == q4.PATH_MFMA else "valu_kernel"
         del c
         torch.cuda.synchronize()
 
     @staticmethod
-    def algorithmic_bytes(name, nb):
-        """Weights + staged activations read + outputs written by one GEMV launch."""
+    def algorithmic_bytes(name, nb, fused=False):
+        """Weights + activations read (f32 x for the fused launch, else the prepared f16
+        streams and chunk sums) + outputs written by one GEMV launch."""
         import workloads
         w = workloads.WORKLOADS[name]
         n_mat, out_dim, in_dim = w["n_mat"], w["out_dim"], w["in_dim"]
         rows = n_mat * nb
-        return (workloads.weight_bytes(n_mat, out_dim, in_dim)
-                + rows * (in_dim * 2 + in_dim // 32 * 4) + rows * out_dim * 4)
+        xbytes = in_dim * 4 if fused else in_dim * 2 + in_dim // 32 * 4
+        return workloads.weight_bytes(n_mat, out_dim, in_dim) + rows * xbytes + rows * out_dim * 4
 
     def prep(self):
-        self.q4.q4mv_prepare_x(self.x, self.xe, self.xo, self.xsum)
+        if not self.fused:  # the fused launch does the prep itself
+            self.q4.q4mv_prepare_x(self.x, self.xe, self.xo, self.xsum)
 
     def gemv(self, i):
         k = i % self.R
-        if self.bits != 4:
+        if self.fused:
+            self.q4.q4mv_fused(self.w[k], self.s[k], self.b[k], self.x, self.nb, y=self.y)
+        elif self.bits != 4:
             self.q4.q4mv_lowbit(self.bits, self.w[k], self.s[k], self.b[k], self.xe, self.xo,
                                 self.xsum, self.nb, y=self.y)
         elif self.silu_div is not None:
@@ -166,7 +173,8 @@ class Problem:
         return statistics.median(ts)
 
     def check_graph_output(self):
-        """The graph's result equals an eager call bit for bit (weights copies are equal)."""
+        """The graph's result equals an eager call bit for bit (weights copies are equal);
+        a fused step's also equals q4mv_prepare_x + q4mv."""
         torch = self.torch
         got = self.y.clone()
         self.prep()
@@ -174,6 +182,12 @@ class Problem:
         torch.cuda.synchronize()
         if not torch.equal(got, self.y):
             raise RuntimeError("graph replay output differs from the eager call")
+        if self.fused:
+            xe, xo, xsum = self.q4.q4mv_prepare_x(self.x)
+            two = self.q4.q4mv(self.w[0], self.s[0], self.b[0], xe, xo, xsum, self.nb)
+            torch.cuda.synchronize()
+            if not torch.equal(got, two):
+                raise RuntimeError("fused step differs from q4mv_prepare_x + q4mv")
 
     def time_steps(self, steps, warmup):
         """ms per full step (prep + GEMV), graph-captured."""
@@ -425,7 +439,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, nb, cmd, out_txt):
             d = {}
     d[f"{workload}_nb{nb}"] = entry
     json.dump(d, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
-    p = Problem.algorithmic_bytes(workload, nb)
+    p = Problem.algorithmic_bytes(workload, nb, fused=True)  # pmc_probe runs q4mv_fused
     lines = [f"# HBM traffic of {kname.split('(')[0]} on {workload} NB={nb}",
              f"# command (twice, COUNTER = FETCH_SIZE, then WRITE_SIZE): {cmd}",
              f"calibration kernel (torch neg, {CALIB_BYTES} B read + {CALIB_BYTES} B written): "
@@ -449,7 +463,7 @@ def pmc_probe(workload, nb):
         torch.neg(src, out=dst)  # one kernel that reads and writes exactly CALIB_BYTES
     torch.cuda.synchronize()
     del src, dst
-    p = Problem(workload, nb)
+    p = Problem(workload, nb, fused=True)
     for i in range(10):
         p.gemv(i)
     torch.cuda.synchronize()
@@ -491,13 +505,15 @@ def main():
     if args.pmc_probe:
         return pmc_probe(args.workload, args.nb)
 
-    prob = Problem(args.workload, args.nb)
+    prob = Problem(args.workload, args.nb, fused=True)
     if args.eager:
         step_ms = prob.time_eager(args.steps, args.warmup)
         kern_ms = step_ms
     else:
         step_ms = prob.time_steps(args.steps, args.warmup)
-        kern_ms = prob.time_kernel(args.steps)
+        # a fused step is exactly one launch of the GEMV kernel: its timed region is the
+        # kernel's (HIP events around the graph of back-to-back launches on the launch stream)
+        kern_ms = step_ms if prob.fused else prob.time_kernel(args.steps)
     value = prob.weight_bytes / (step_ms * 1e-3) / 1e9
     achieved = prob.algo_bytes / (kern_ms * 1e-3) / 1e9
     result = {
@@ -518,7 +534,8 @@ def main():
                    "n_mat": prob.n_mat, "out_dim": prob.out_dim, "in_dim": prob.in_dim,
                    "nb": prob.nb, "group": 64, "weight_bytes": prob.weight_bytes,
                    "rotation_copies": prob.R, "seed": 0, "graph_captured": not args.eager,
-                   "operands": "u4 codes, bf16 scale+bias per 64, f16 activations, f32 acc"},
+                   "operands": "u4 codes, bf16 scale+bias per 64, f16 activations, f32 acc",
+                   "step": "q4mv_fused (activation prep inside the GEMV launch)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "rows_per_s": round(prob.n_mat * prob.out_dim / (step_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
@@ -536,14 +553,20 @@ def main():
         runs = [("lm_head", nb) for nb in (1, 4, 8, 16)] + [("up", nb) for nb in (1, 4, 8)] + \
                [("moe_down", 4), ("dense", 1), ("dense", 4), ("dense", 8)]
         for name, nb in runs:
+            # kernel_us: q4mv on prepared activations; fused_step_us: q4mv_fused (prep
+            # inside, one launch); two_launch_step_us: q4mv_prepare_x + q4mv
             p = Problem(name, nb)
             ms = p.time_kernel(200)
-            gbps = p.weight_bytes / (ms * 1e-3) / 1e9
-            sweep.append({"workload": name, "nb": nb, "kernel_us": round(ms * 1e3, 3),
+            two = p.time_steps(200, 20)
+            p.fused = True
+            fused = p.time_steps(200, 20)
+            gbps = p.weight_bytes / (fused * 1e-3) / 1e9
+            sweep.append({"workload": name, "nb": nb, "fused_step_us": round(fused * 1e3, 3),
                           "weight_GBps": round(gbps, 1),
                           "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
-                          "rows_per_s": round(p.n_mat * p.out_dim / (ms * 1e-3), 1),
-                          "path": p.path})
+                          "rows_per_s": round(p.n_mat * p.out_dim / (fused * 1e-3), 1),
+                          "kernel_us": round(ms * 1e3, 3),
+                          "two_launch_step_us": round(two * 1e3, 3), "path": p.path})
             del p
             torch.cuda.empty_cache()
         # fused epilogues: the silu(y / div) store, and the expert MLP chain
