@@ -61,6 +61,7 @@ def lib():
         L.q4mv_pack_lowbit.argtypes = [i32, p, p, i64, i32, p]
         L.q4mv_lowbit.argtypes = [i32] + [p] * 7 + [i32] * 5 + [p]
         L.q4mv_experts.argtypes = [p, p, p, i32, p, i32, p, p, p, p] + [i32] * 5 + [p]
+        L.q4mv_experts_fused.argtypes = [p, p, p, i32, p, i32, p, p] + [i32] * 6 + [p]
         L.q4mv_combine.argtypes = [p, p, p, i32, i32, i32, p]
         L.q4mv_auto_path.argtypes = [i32, i32, i32, i32]
         L.q4mv_status_str.argtypes = [i32]
@@ -326,6 +327,35 @@ def q4mv_experts(w, scales, biases, sel, xe, xo, xsum, nb, x_shared, path=PATH_A
         w.data_ptr(), scales.data_ptr(), biases.data_ptr(), n_bank, sel.data_ptr(), n_sel,
         xe.data_ptr(), xo.data_ptr(), xsum.data_ptr(), y.data_ptr(), out_dim, in_dim, nb,
         int(bool(x_shared)), int(path), _stream(w, stream)))
+    return y
+
+
+def q4mv_experts_fused(w, scales, biases, sel, x, nb, x_shared, swiglu=False, path=PATH_AUTO,
+                       y=None, stream=None):
+    """:func:`q4mv_experts` with the activation prep inside the launch, from f32 rows x:
+    [rows, in_dim], or with swiglu [rows, 2*in_dim] gate|up rows whose activations are
+    silu(gate)*up (rows = nb when x_shared, else n_sel*nb). Bitwise the two-call result."""
+    torch = _torch()
+    if w.dim() != 3:
+        raise ValueError("w: expected [n_bank, out_dim, in_dim/8]")
+    n_bank, out_dim, w8 = w.shape
+    in_dim = w8 * 8
+    _need(w, torch.int32, (n_bank, out_dim, w8), "w")
+    _need(scales, torch.bfloat16, (n_bank, out_dim, in_dim // 64), "scales")
+    _need(biases, torch.bfloat16, (n_bank, out_dim, in_dim // 64), "biases")
+    if sel.dim() != 1:
+        raise ValueError("sel: expected [n_sel]")
+    n_sel = sel.shape[0]
+    _need(sel, torch.int32, (n_sel,), "sel")
+    rows = nb if x_shared else n_sel * nb
+    _need(x, torch.float32, (rows, 2 * in_dim if swiglu else in_dim), "x")
+    if y is None:
+        y = torch.empty((n_sel, nb, out_dim), dtype=torch.float32, device=w.device)
+    _need(y, torch.float32, (n_sel, nb, out_dim), "y")
+    _check("q4mv_experts_fused", lib().q4mv_experts_fused(
+        w.data_ptr(), scales.data_ptr(), biases.data_ptr(), n_bank, sel.data_ptr(), n_sel,
+        x.data_ptr(), y.data_ptr(), out_dim, in_dim, nb, int(bool(x_shared)),
+        int(bool(swiglu)), int(path), _stream(w, stream)))
     return y
 
 

@@ -125,6 +125,36 @@ static int run_path(const uint32_t *w, const uint16_t *scales, const uint16_t *b
     return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
 }
 
+// Shared body of q4mv_experts and q4mv_experts_fused (activations as prepared streams, or
+// as f32 rows xf when xf is non-null; those pointers are checked by the callers).
+static int run_experts(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                       int n_bank, const int32_t *sel, int n_sel, const void *xe,
+                       const void *xo, const float *xsum, const float *xf, int xf_glu,
+                       float *y, int out_dim, int in_dim, int nb, int x_shared, int path,
+                       void *stream)
+{
+    if (!w || !scales || !biases || !sel || !y) return Q4MV_ERR_NULL;
+    if (n_bank < 1 || n_sel < 1 || n_sel > 65535 || out_dim < 1 || in_dim < 64 ||
+        in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB ||
+        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(sel, 4) ||
+        !aligned(y, 4))
+        return Q4MV_ERR_ALIGN;
+    if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
+    if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
+    if (path < 0) return path;
+    if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
+    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_sel * ((out_dim + 31) / 32)).wpb == 0)
+        return Q4MV_ERR_SHAPE;
+    GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_sel, out_dim, in_dim, nb, 0.0f,
+               static_cast<hipStream_t>(stream), sel, n_bank, x_shared != 0};
+    a.xf = xf;
+    a.xf_glu = xf_glu;
+    hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
+    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+}
+
 extern "C" {
 
 int q4mv_pack_codes(const uint8_t *codes, uint32_t *w, int64_t n_codes, void *stream)
@@ -203,24 +233,22 @@ int q4mv_experts(const uint32_t *w, const uint16_t *scales, const uint16_t *bias
                  const float *xsum, float *y, int out_dim, int in_dim, int nb, int x_shared,
                  int path, void *stream)
 {
-    if (!w || !scales || !biases || !sel || !xe || !xo || !xsum || !y) return Q4MV_ERR_NULL;
-    if (n_bank < 1 || n_sel < 1 || n_sel > 65535 || out_dim < 1 || in_dim < 64 ||
-        in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB ||
-        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
-        return Q4MV_ERR_SHAPE;
-    if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(sel, 4) ||
-        !aligned(xe, 16) || !aligned(xo, 16) || !aligned(xsum, 4) || !aligned(y, 4))
-        return Q4MV_ERR_ALIGN;
-    if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
-    if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
-    if (path < 0) return path;
-    if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
-    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_sel * ((out_dim + 31) / 32)).wpb == 0)
-        return Q4MV_ERR_SHAPE;
-    GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_sel, out_dim, in_dim, nb, 0.0f,
-               static_cast<hipStream_t>(stream), sel, n_bank, x_shared != 0};
-    hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
-    return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
+    if (!xe || !xo || !xsum) return Q4MV_ERR_NULL;
+    if (!aligned(xe, 16) || !aligned(xo, 16) || !aligned(xsum, 4)) return Q4MV_ERR_ALIGN;
+    return run_experts(w, scales, biases, n_bank, sel, n_sel, xe, xo, xsum, nullptr, 0, y,
+                       out_dim, in_dim, nb, x_shared, path, stream);
+}
+
+int q4mv_experts_fused(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                       int n_bank, const int32_t *sel, int n_sel, const float *x, float *y,
+                       int out_dim, int in_dim, int nb, int x_shared, int swiglu, int path,
+                       void *stream)
+{
+    if (!x) return Q4MV_ERR_NULL;
+    if (!aligned(x, 16)) return Q4MV_ERR_ALIGN;
+    if (swiglu != 0 && swiglu != 1) return Q4MV_ERR_VALUE;
+    return run_experts(w, scales, biases, n_bank, sel, n_sel, nullptr, nullptr, nullptr, x,
+                       swiglu, y, out_dim, in_dim, nb, x_shared, path, stream);
 }
 
 int q4mv_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows, int in_dim,

@@ -79,6 +79,46 @@ __device__ __forceinline__ uint4 make_pairs(uint2 e, uint2 o)
     return p;
 }
 
+// silu(g) * u in f32 (fn_moe_act_b, Constant BATCH_MSL page): g / (1 + e^-g) * u, with the
+// product rounded to f32 before any later conversion. The empty asm keeps the compiler from
+// merging the product with a following f32 -> f16 conversion into one mixed-precision FMA
+// (v_fma_mixlo_f16), which rounds the exact product to f16 once and so differs from
+// f16(f32(product)) when the f32 product falls on an f16 rounding midpoint.
+__device__ __forceinline__ float swiglu_f32(float g, float u)
+{
+    float h = g / (1.0f + expf(-g)) * u;
+    asm("" : "+v"(h));
+    return h;
+}
+
+// One 8-column word of f32 activations for the prep done inside the GEMV: a plain row
+// (glu = 0, rows of in_dim values) or a [gate | up] row of 2*in_dim values whose word is
+// silu(gate) * up (glu = 1), formed as the SwiGLU prep forms it (swiglu_f32). row points at
+// the row's first float4.
+__device__ __forceinline__ void xword_load(const float4 *row, int kw, int in_dim, int glu,
+                                           float4 (&v)[4])
+{
+    v[0] = row[2 * kw];
+    v[1] = row[2 * kw + 1];
+    if (glu) {
+        v[2] = row[(in_dim >> 2) + 2 * kw];
+        v[3] = row[(in_dim >> 2) + 2 * kw + 1];
+    }
+}
+
+__device__ __forceinline__ void xword_values(const float4 (&v)[4], int glu, float (&f)[8])
+{
+    const float g[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+    if (glu) {
+        const float u[8] = {v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+#pragma unroll
+        for (int t = 0; t < 8; t++) f[t] = swiglu_f32(g[t], u[t]);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; t++) f[t] = g[t];
+    }
+}
+
 // DPP helpers (row = 16 lanes). quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
 // row_half_mirror = 0x141, row_mirror = 0x140.
 template <int CTRL>

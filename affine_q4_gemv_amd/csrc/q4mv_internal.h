@@ -28,6 +28,8 @@ struct GemvArgs {
     // f32 activations [rows][in_dim] (rows as for xe): the kernels stage them with the prep
     // done in the block (xe, xo and xsum are then not read).
     const float *xf = nullptr;
+    // xf rows are [gate | up] (2*in_dim values) and the activations silu(gate) * up.
+    int xf_glu = 0;
 };
 
 // Kernel paths (same numbering as q4mv_path in q4mv.h).

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
     int out_dim, int in_dim, int nb, float epi_div, const int *__restrict__ sel,
-    int n_bank, int x_shared, const float *__restrict__ xf)
+    int n_bank, int x_shared, const float *__restrict__ xf, int xf_glu)
 {
     constexpr int TH = WPB * 64;
     constexpr int TPB = WPB / KS;  // tile groups per block
@@ -142,28 +142,30 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // pairs, two quad DPP steps add the chunk's four words; then a group's two chunks in
     // order), so the LDS contents are bitwise those staged from q4mv_prepare_x's outputs.
     // One thread per 8-column word; a quad of lanes is one chunk, 8 lanes one group (words
-    // per row are a multiple of 8).
+    // per row are a multiple of 8). With xf_glu the rows are [gate | up] and the values
+    // silu(gate) * up (as q4mv_swiglu_prep forms them).
     auto fstage = [&]() {
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
-        const float4 *xf_m = reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)(in_dim >> 2);
+        const int rs4 = xf_glu ? in_dim >> 1 : in_dim >> 2;  // float4 per row
+        const float4 *xf_m = reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4;
         const int wrow = in_dim >> 3, words = nb * wrow;
         float *xsw = reinterpret_cast<float *>(xsg_w);
         const _Float16 sixteenth = (_Float16)0.0625f;
         for (int base = threadIdx.x; base < words; base += 2 * TH) {
-            float4 v[2][2];
+            float4 v[2][4];
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 const int wi = min(base + i * TH, words - 1);
-                v[i][0] = xf_m[2 * wi];
-                v[i][1] = xf_m[2 * wi + 1];
+                const int r = wi / wrow;
+                xword_load(xf_m + (size_t)r * rs4, wi - r * wrow, in_dim, xf_glu, v[i]);
             }
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 const int wi = base + i * TH;
                 if (wi < words) {  // uniform per 8 lanes
                     const int r = wi / wrow, kw = wi - r * wrow;
-                    const float f[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w,
-                                        v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
+                    float f[8];
+                    xword_values(v[i], xf_glu, f);
                     _Float16 h[8];
 #pragma unroll
                     for (int t = 0; t < 8; t++) h[t] = (_Float16)f[t];
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 
 typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, float,
-                       const int *, int, int, const float *);
+                       const int *, int, int, const float *, int);
 
 static bool use_mf16(int ks, int nb, long tiles)
 {
@@ -612,7 +614,7 @@ hipError_t launch_mfma(const GemvArgs &a)
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
                        a.xsum, a.y, a.out_dim, a.in_dim, a.nb, a.epi_div, a.sel, a.n_bank, a.x_shared,
-                       a.xf);
+                       a.xf, a.xf_glu);
     return hipGetLastError();
 }
 

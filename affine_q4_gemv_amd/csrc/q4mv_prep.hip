@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256) void swiglu_prep_kernel(const float2 *__restri
     const int64_t row = i / half_inter, k = i - row * half_inter;
     const float2 g = gu[row * (2 * half_inter) + k];               // gate[2k], gate[2k+1]
     const float2 u = gu[row * (2 * half_inter) + half_inter + k];  // up[2k], up[2k+1]
-    const float he = g.x / (1.0f + expf(-g.x)) * u.x;
-    const float ho = g.y / (1.0f + expf(-g.y)) * u.y;
+    const float he = swiglu_f32(g.x, u.x);
+    const float ho = swiglu_f32(g.y, u.y);
     const _Float16 a = (_Float16)he, b = (_Float16)ho;
     xe[i] = a;
     xo[i] = b;

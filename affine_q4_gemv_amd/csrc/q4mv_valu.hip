@@ -235,7 +235,8 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
     int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt, float epi_div,
-    const int *__restrict__ sel, int n_bank, int x_shared, const float *__restrict__ xf)
+    const int *__restrict__ sel, int n_bank, int x_shared, const float *__restrict__ xf,
+    int xf_glu)
 {
     const int log2g = LOG2G >= 0 ? LOG2G : log2g_rt;
     extern __shared__ uint4 lds[];
@@ -295,16 +296,18 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
     // adds its word's four pairs, two quad DPP steps add the chunk's four words), so the
     // staged LDS contents are bitwise those staged from q4mv_prepare_x's outputs. One thread
     // per 8-column word; a quad of lanes is one chunk (words per row are a multiple of 8).
-    const int words = NB * (in_dim >> 3);
-    const float4 *xf_m = xf ? reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)(in_dim >> 2)
-                            : nullptr;
-    struct FStage { float4 v[2][2]; };
+    // With xf_glu the rows are [gate | up] and the values silu(gate) * up (as
+    // q4mv_swiglu_prep forms them).
+    const int wrow = in_dim >> 3, words = NB * wrow;
+    const int rs4 = xf_glu ? in_dim >> 1 : in_dim >> 2;  // float4 per row
+    const float4 *xf_m = xf ? reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4 : nullptr;
+    struct FStage { float4 v[2][4]; };
     auto fstage_load = [&](int base, FStage &st) {
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const int wi = min(base + i * kValuThreads, words - 1);
-            st.v[i][0] = xf_m[2 * wi];
-            st.v[i][1] = xf_m[2 * wi + 1];
+            const int r = wi / wrow;
+            xword_load(xf_m + (size_t)r * rs4, wi - r * wrow, in_dim, xf_glu, st.v[i]);
         }
     };
     auto fstage_store = [&](int base, const FStage &st) {
@@ -312,9 +315,9 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
         for (int i = 0; i < 2; i++) {
             const int wi = base + i * kValuThreads;
             if (wi < words) {  // uniform per quad
-                const int r = wi / (in_dim >> 3), kw = wi - r * (in_dim >> 3);
-                const float f[8] = {st.v[i][0].x, st.v[i][0].y, st.v[i][0].z, st.v[i][0].w,
-                                    st.v[i][1].x, st.v[i][1].y, st.v[i][1].z, st.v[i][1].w};
+                const int r = wi / wrow, kw = wi - r * wrow;
+                float f[8];
+                xword_values(st.v[i], xf_glu, f);
                 _Float16 h[8];
 #pragma unroll
                 for (int t = 0; t < 8; t++) h[t] = (_Float16)f[t];
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
 
 typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, int, int, int,
-                       float, const int *, int, int, const float *);
+                       float, const int *, int, int, const float *, int);
 
 // (log2 G, CPL) of the specialised row lengths: in_dim = 32 * CPL << log2G.
 #define Q4MV_VALU_SHAPES(X)                                                                   \
@@ -799,7 +802,7 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
                        a.xsum, a.y, a.out_dim, a.in_dim, a.nb, r0, log2g, cpl, a.epi_div,
-                       a.sel, a.n_bank, a.x_shared, a.xf);
+                       a.sel, a.n_bank, a.x_shared, a.xf, a.xf_glu);
     return hipGetLastError();
 }
 

@@ -251,6 +251,9 @@ class MoeChain(Problem):
         self.sets = [(w1, s1, b1, w2, s2, b2)] + [
             tuple(t.clone() for t in (w1, s1, b1, w2, s2, b2)) for _ in range(self.R - 1)]
         x = torch.from_numpy(up["x"].reshape(n_mat * nb, hidden)).to(dev)
+        self.x = x
+        self.fused = False
+        self.ids = torch.arange(n_mat, dtype=torch.int32, device=dev)
         self.xe, self.xo, self.xsum = q4.q4mv_prepare_x(x)
         self.gu = torch.empty((n_mat, nb, 2 * inter), dtype=torch.float32, device=dev)
         self.xe2 = torch.empty((n_mat * nb, inter // 2), dtype=torch.float16, device=dev)
@@ -266,6 +269,12 @@ class MoeChain(Problem):
     def gemv(self, i):
         w1, s1, b1, w2, s2, b2 = self.sets[i % self.R]
         q4 = self.q4
+        if self.fused:
+            # gate|up with the prep inside, down with the SwiGLU inside (two launches)
+            q4.q4mv_fused(w1, s1, b1, self.x, self.nb, y=self.gu)
+            q4.q4mv_experts_fused(w2, s2, b2, self.ids, self.gu.view(-1, 2 * self.inter),
+                                  self.nb, False, swiglu=True, y=self.y)
+            return
         q4.q4mv(w1, s1, b1, self.xe, self.xo, self.xsum, self.nb, y=self.gu)
         q4.q4mv_swiglu_prep(self.gu.view(self.n_mat * self.nb, 2 * self.inter), self.xe2,
                             self.xo2, self.xsum2)
@@ -316,6 +325,7 @@ class MoeLayer(MoeChain):
             tuple(t.clone() for t in (w1, s1, b1, w2, s2, b2)) for _ in range(self.R - 1)]
         self.sel = torch.from_numpy(sel).to(dev)
         self.wmap = torch.from_numpy(wmap).to(dev)
+        self.fused = False
         self.x = torch.from_numpy(np.ascontiguousarray(gu["x"][0])).to(dev)
         self.xe = torch.empty((nb, hidden // 2), dtype=torch.float16, device=dev)
         self.xo = torch.empty_like(self.xe)
@@ -332,6 +342,14 @@ class MoeLayer(MoeChain):
     def gemv(self, i):
         w1, s1, b1, w2, s2, b2 = self.sets[i % self.R]
         q4, nb = self.q4, self.nb
+        if self.fused:
+            # three launches: gate|up from the f32 token rows, down with the SwiGLU inside,
+            # combine
+            q4.q4mv_experts_fused(w1, s1, b1, self.sel, self.x, nb, True, y=self.gu)
+            q4.q4mv_experts_fused(w2, s2, b2, self.sel, self.gu.view(self.n_u * nb, 2 * self.inter),
+                                  nb, False, swiglu=True, y=self.yd)
+            q4.q4mv_combine(self.yd, self.wmap, out=self.y)
+            return
         q4.q4mv_prepare_x(self.x, self.xe, self.xo, self.xsum)
         q4.q4mv_experts(w1, s1, b1, self.sel, self.xe, self.xo, self.xsum, nb, True, y=self.gu)
         q4.q4mv_swiglu_prep(self.gu.view(self.n_u * nb, 2 * self.inter), self.xe2, self.xo2,
@@ -615,26 +633,34 @@ def main():
                       "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)})
         del wf
         torch.cuda.empty_cache()
-        p = MoeChain()
-        ms = p.time_kernel(200)
-        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
-        sweep.append({"workload": "moe_mlp 8x(2560->2x640->2560)", "nb": 4,
-                      "launches": "gate|up GEMV + SwiGLU prep + down GEMV",
-                      "step_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
-                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
-        del p
-        torch.cuda.empty_cache()
-        p = MoeLayer()
-        ms = p.time_kernel(200)
-        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
-        sweep.append({"workload": f"moe_layer top-8 of 32 experts (2560->2x640->2560), "
-                                  f"{p.n_u} routed", "nb": 4,
-                      "launches": "prep + gate|up experts + SwiGLU prep + down experts + "
-                                  "combine",
-                      "step_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
-                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
-        del p
-        torch.cuda.empty_cache()
+        for fused in (False, True):
+            p = MoeChain()
+            p.fused = fused
+            ms = p.time_kernel(200)
+            gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+            sweep.append({"workload": "moe_mlp 8x(2560->2x640->2560)", "nb": 4,
+                          "launches": "q4mv_fused gate|up + down experts with the SwiGLU "
+                                      "inside" if fused else
+                                      "gate|up GEMV + SwiGLU prep + down GEMV",
+                          "step_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
+                          "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
+            del p
+            torch.cuda.empty_cache()
+        for fused in (False, True):
+            p = MoeLayer()
+            p.fused = fused
+            ms = p.time_kernel(200)
+            gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+            sweep.append({"workload": f"moe_layer top-8 of 32 experts (2560->2x640->2560), "
+                                      f"{p.n_u} routed", "nb": 4,
+                          "launches": "gate|up experts from f32 rows + down experts with the "
+                                      "SwiGLU inside + combine" if fused else
+                                      "prep + gate|up experts + SwiGLU prep + down experts + "
+                                      "combine",
+                          "step_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
+                          "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
+            del p
+            torch.cuda.empty_cache()
         result["sweep"] = sweep
 
     if not args.no_cpu:

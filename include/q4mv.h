@@ -257,6 +257,25 @@ int q4mv_experts(const uint32_t *w, const uint16_t *scales, const uint16_t *bias
                  int path, void *stream);
 
 /*
+ * q4mv_experts_fused -- q4mv_experts with the activation prep done inside the launch, from
+ * f32 rows (as q4mv_fused does for q4mv):
+ *   x      : f32, 16-byte aligned. swiglu = 0: rows of in_dim values, [nb][in_dim] when
+ *            x_shared, else [n_sel*nb][in_dim] (slot u reads rows u*nb .. u*nb+nb-1);
+ *            swiglu = 1: [gate | up] rows of 2*in_dim values in the same arrangement (the
+ *            stacked output of the gate|up projection), and the activations are
+ *            silu(gate) * up formed in f32 as q4mv_swiglu_prep forms them (fn_moe_act_b,
+ *            Constant BATCH_MSL page: the SwiGLU of the expert MLP folded into the down
+ *            projection's launch).
+ * Other arguments and errors as q4mv_experts, plus VALUE for swiglu outside {0, 1}. The
+ * result is bitwise what q4mv_prepare_x (or q4mv_swiglu_prep) followed by q4mv_experts
+ * gives on the same path.
+ */
+int q4mv_experts_fused(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                       int n_bank, const int32_t *sel, int n_sel, const float *x, float *y,
+                       int out_dim, int in_dim, int nb, int x_shared, int swiglu, int path,
+                       void *stream);
+
+/*
  * q4mv_combine -- routing-weighted sum of expert outputs (the expert sum of
  * fn_moe_combine_b on the Constant BATCH_MSL page, without its shared-expert gate):
  *   y    : f32 [n_u][nb][out_dim]   e.g. q4mv_experts output

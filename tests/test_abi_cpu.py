@@ -30,7 +30,7 @@ def test_header_declares_expected_entry_points():
     for name in ("q4mv_prepare_x", "q4mv", "q4mv_2row", "q4mv_pack_codes", "q4mv_path",
                  "q4mv_silu", "q4mv_path_silu", "q4mv_swiglu_prep", "q4mv_auto_path",
                  "q4mv_quantize", "q4mv_experts", "q4mv_combine", "q4mv_pack_lowbit",
-                 "q4mv_lowbit", "q4mv_fused",
+                 "q4mv_lowbit", "q4mv_fused", "q4mv_experts_fused",
                  "q4mv_status_str", "q4mv_version"):
         assert name in fns
 
@@ -236,3 +236,23 @@ def test_fused_validation(L):
         assert L.q4mv_fused(*args(**kw)) == EALIGN, kw
     assert L.q4mv_fused(*args(path=4)) == EPATH
     assert L.q4mv_fused(*args(out=7, path=2)) == EODD
+
+
+def test_experts_fused_validation(L):
+    """q4mv_experts_fused: f32 x (16-byte aligned), swiglu 0 or 1; the rest as q4mv_experts."""
+    def args(**kw):
+        a = dict(w=A, s=A, b=A, n_bank=4, sel=A, n_sel=2, x=A, y=A, out=8, ind=128, nb=1,
+                 shared=1, swiglu=0, path=0)
+        a.update(kw)
+        return [a["w"], a["s"], a["b"], a["n_bank"], a["sel"], a["n_sel"], a["x"], a["y"],
+                a["out"], a["ind"], a["nb"], a["shared"], a["swiglu"], a["path"], None]
+    for k in ("w", "s", "b", "sel", "x", "y"):
+        assert L.q4mv_experts_fused(*args(**{k: None})) == ENULL
+    for kw in (dict(n_bank=0), dict(n_sel=0), dict(n_sel=65536), dict(out=0), dict(ind=96),
+               dict(nb=17)):
+        assert L.q4mv_experts_fused(*args(**kw)) == ESHAPE, kw
+    for kw in (dict(x=A + 8), dict(sel=A + 2), dict(w=A + 4)):
+        assert L.q4mv_experts_fused(*args(**kw)) == EALIGN, kw
+    assert L.q4mv_experts_fused(*args(swiglu=2)) == EVALUE
+    assert L.q4mv_experts_fused(*args(path=5)) == EPATH
+    assert L.q4mv_experts_fused(*args(out=7, path=2)) == EODD

@@ -71,3 +71,82 @@ def test_fused_lm_head(nb):
     got = q4.q4mv_fused(d["w"], d["s"], d["b"], d["x"], nb)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+# ---- routed experts with the prep (and the SwiGLU of the expert MLP) inside the launch
+
+def same_bits(a, b):
+    """Equal bit patterns (NaN rows of out-of-bank ids compare equal too)."""
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def expert_bank(n_bank, out_dim, in_dim, seed):
+    case = workloads.make_shape(n_bank, out_dim, in_dim, 1, seed=seed)
+    d = upload(case)
+    return d["w"], d["s"], d["b"]
+
+
+# (n_bank, out_dim, in_dim, nb, sel): the MoE gate/up and down shapes, odd rows, the MFMA
+# range, repeated and unordered ids and one outside the bank (NaN rows)
+EXPERTS = [(6, 1280, 2560, 4, [5, 1, 1, 0, 3]), (6, 2560, 640, 4, [2, 4, 0, 9]),
+           (3, 77, 256, 1, [2, 0, 2, 1]), (4, 96, 512, 16, [3, 3, 0])]
+EXP_PATHS = [q4.PATH_AUTO, q4.PATH_VALU, q4.PATH_MFMA, q4.PATH_VALU_2ROW]
+
+
+@pytest.mark.parametrize("case", EXPERTS, ids=[f"{c[0]}x{c[1]}x{c[2]}-nb{c[3]}" for c in EXPERTS])
+def test_experts_fused_equals_two_calls(case):
+    n_bank, out_dim, in_dim, nb, sel = case
+    w, s, b = expert_bank(n_bank, out_dim, in_dim, seed=60 + nb)
+    sel_d = torch.tensor(sel, dtype=torch.int32, device="cuda")
+    n_sel = len(sel)
+    rng = np.random.default_rng(nb)
+    for shared in (True, False):
+        rows = nb if shared else n_sel * nb
+        x = torch.from_numpy(rng.standard_normal((rows, in_dim)).astype(np.float32)).cuda()
+        xe, xo, xsum = q4.q4mv_prepare_x(x)
+        # gate|up rows of the same slots for the SwiGLU form
+        gu = torch.from_numpy(
+            (2 * rng.standard_normal((rows, 2 * in_dim))).astype(np.float32)).cuda()
+        he, ho, hsum = q4.q4mv_swiglu_prep(gu)
+        for path in EXP_PATHS:
+            if path == q4.PATH_VALU_2ROW and out_dim % 2:
+                continue
+            flush(f"[experts fused] {case} shared={shared} path={path}")
+            want = q4.q4mv_experts(w, s, b, sel_d, xe, xo, xsum, nb, shared, path)
+            got = q4.q4mv_experts_fused(w, s, b, sel_d, x, nb, shared, False, path)
+            want_g = q4.q4mv_experts(w, s, b, sel_d, he, ho, hsum, nb, shared, path)
+            got_g = q4.q4mv_experts_fused(w, s, b, sel_d, gu, nb, shared, True, path)
+            torch.cuda.synchronize()
+            assert same_bits(got, want), f"{case} shared={shared} path={path}"
+            assert same_bits(got_g, want_g), f"{case} swiglu shared={shared} path={path}"
+
+
+def test_moe_layer_fused_equals_five_launches():
+    """The decode MoE layer (4 tokens, top-8 of 32 experts, hidden 2560, intermediate 640)
+    in three launches -- gate|up over the routed experts from the f32 token rows, the down
+    projection with the SwiGLU in its staging, the combine -- bitwise equal to the five-launch
+    chain (prep, gate|up, SwiGLU prep, down, combine) that the oracle chain checks."""
+    n_exp, hidden, inter, nb, top_k = 32, 2560, 640, 4, 8
+    sel, wmap = workloads.make_routing(nb, n_exp, top_k, seed=71)
+    n_u = sel.size
+    gu_bank = workloads.make_shape(n_exp, 2 * inter, hidden, nb, seed=72)
+    dn_bank = workloads.make_weights(n_exp, hidden, inter, seed=73)
+    d1 = upload(gu_bank)
+    w1, s1, b1 = d1["w"], d1["s"], d1["b"]
+    w2 = q4.q4mv_pack_codes(torch.from_numpy(dn_bank[0]).cuda())
+    from q4_gpu import bf16_tensor
+    s2, b2 = bf16_tensor(dn_bank[1]), bf16_tensor(dn_bank[2])
+    sel_d, wmap_d = torch.from_numpy(sel).cuda(), torch.from_numpy(wmap).cuda()
+    x = torch.from_numpy(np.ascontiguousarray(gu_bank["x"][0])).cuda()
+    flush(f"[moe layer fused] {n_u} routed experts of {n_exp}")
+    xe, xo, xsum = q4.q4mv_prepare_x(x)
+    gu = q4.q4mv_experts(w1, s1, b1, sel_d, xe, xo, xsum, nb, True)
+    xe2, xo2, xsum2 = q4.q4mv_swiglu_prep(gu.view(n_u * nb, 2 * inter))
+    y = q4.q4mv_experts(w2, s2, b2, sel_d, xe2, xo2, xsum2, nb, False)
+    out = q4.q4mv_combine(y, wmap_d)
+    gu_f = q4.q4mv_experts_fused(w1, s1, b1, sel_d, x, nb, True)
+    y_f = q4.q4mv_experts_fused(w2, s2, b2, sel_d, gu_f.view(n_u * nb, 2 * inter), nb, False,
+                                swiglu=True)
+    out_f = q4.q4mv_combine(y_f, wmap_d)
+    torch.cuda.synchronize()
+    assert torch.equal(gu_f, gu) and torch.equal(y_f, y) and torch.equal(out_f, out)
