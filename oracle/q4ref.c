@@ -25,7 +25,7 @@
  * qwen4exp_gpu.rs page, NgramTable bf16 row read). The decode is exact.
  *
  * bound[m][r][o] = sum_i ( |S q x| + |B x| ) over the in_dim columns of that output, the
- * magnitude against which the per-element error of a faster evaluation is judged.
+ * magnitude against which the per-element error of a faster evaluation is checked.
  *
  * Layouts (all row-major, contiguous):
  *   q  u8  [n_mat][out_dim][in_dim]         x  f32 [n_mat][nb][in_dim]

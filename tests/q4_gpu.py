@@ -1,5 +1,5 @@
 """Helpers for the GPU tests: move generated inputs to the device through the library's own
-entry points, run a kernel path, and judge parity against the oracle."""
+entry points, run a kernel path, and check parity against the oracle."""
 import numpy as np
 import torch
 

@@ -62,8 +62,10 @@ def test_fused_ragged(shape):
 
 
 @pytest.mark.parametrize("nb", [1, 16])
-def test_fused_lm_head(nb):
-    """The full LM head in the launch configuration the benchmark times."""
+def test_fused_lm_head(oracle_lib, nb):
+    """The full LM head in the launch configuration the benchmark times: bitwise the
+    two-call result, and within the tolerance of the oracle on sampled rows (the first and
+    last 128 and random ones, computed one by one)."""
     case = workloads.make_case("lm_head", nb=nb)
     d = upload(case)
     flush(f"[fused] lm_head nb={nb}")
@@ -71,6 +73,13 @@ def test_fused_lm_head(nb):
     got = q4.q4mv_fused(d["w"], d["s"], d["b"], d["x"], nb)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+    out = case["out_dim"]
+    rng = np.random.default_rng(100 + nb)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(out - 128, out),
+                                     rng.integers(0, out, 1792)]))
+    y_ref, bound = oracle_lib.gemv_rows(case["codes"], case["scales"], case["biases"],
+                                        case["x"], np.zeros_like(rows), rows)
+    parity(got[0].cpu().numpy()[:, rows].T, y_ref, bound, f"fused lm_head nb={nb}")
 
 
 # ---- routed experts with the prep (and the SwiGLU of the expert MLP) inside the launch
