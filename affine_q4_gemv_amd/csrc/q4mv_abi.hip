@@ -93,17 +93,28 @@ using namespace q4mv_impl;
 
 static inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Checks shared by every GEMV entry point: weights, output and shape.
+static int check_weights(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                         float *y, int n_mat, int out_dim, int in_dim, int nb)
+{
+    if (!w || !scales || !biases || !y) return Q4MV_ERR_NULL;
+    if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
+        nb > Q4MV_MAX_NB || (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        return Q4MV_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(y, 4))
+        return Q4MV_ERR_ALIGN;
+    return Q4MV_OK;
+}
+
+// ... plus the prepared activations.
 static int check_gemv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
                       const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
                       int out_dim, int in_dim, int nb)
 {
-    if (!w || !scales || !biases || !xe || !xo || !xsum || !y) return Q4MV_ERR_NULL;
-    if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
-        nb > Q4MV_MAX_NB || (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
-        return Q4MV_ERR_SHAPE;
-    if (!aligned(w, 16) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(scales, 2) ||
-        !aligned(biases, 2) || !aligned(xsum, 4) || !aligned(y, 4))
-        return Q4MV_ERR_ALIGN;
+    if (!xe || !xo || !xsum) return Q4MV_ERR_NULL;
+    const int st = check_weights(w, scales, biases, y, n_mat, out_dim, in_dim, nb);
+    if (st != Q4MV_OK) return st;
+    if (!aligned(xe, 16) || !aligned(xo, 16) || !aligned(xsum, 4)) return Q4MV_ERR_ALIGN;
     return Q4MV_OK;
 }
 
@@ -190,8 +201,7 @@ int q4mv_fused(const uint32_t *w, const uint16_t *scales, const uint16_t *biases
                void *stream)
 {
     if (!x) return Q4MV_ERR_NULL;
-    // xe, xo, xsum are not read: stand-ins that pass the shared checks
-    int st = check_gemv(w, scales, biases, w, w, y, y, n_mat, out_dim, in_dim, nb);
+    const int st = check_weights(w, scales, biases, y, n_mat, out_dim, in_dim, nb);
     if (st != Q4MV_OK) return st;
     if (!aligned(x, 16)) return Q4MV_ERR_ALIGN;
     if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;

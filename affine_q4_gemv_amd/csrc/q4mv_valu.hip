@@ -44,14 +44,9 @@ constexpr bool kValuPrefetch = Q4MV_VALU_PREFETCH != 0;
 #ifndef Q4MV_VALU_XREG_MAX
 #define Q4MV_VALU_XREG_MAX 5
 #endif
-// Output rows per lane group in the paired kernel (2; 4 also gives the same bits).
 // Weights are read with non-temporal loads (each byte is used once; measured faster).
-// With activations in registers, load them straight from device memory (no LDS staging).
-// Measured slower on MI355X (LM head NB=1 43 us against 36.5 us), so off.
-#ifndef Q4MV_VALU_XDIRECT
-#define Q4MV_VALU_XDIRECT 0
-#endif
-constexpr bool kValuXDirect = Q4MV_VALU_XDIRECT != 0;
+// (Activations loaded straight from device memory into registers, with no LDS staging,
+// measured slower on MI355X: LM head NB=1 43 us against 36.5 us.)
 #ifndef Q4MV_VALU_NT
 #define Q4MV_VALU_NT 1
 #endif
@@ -73,6 +68,7 @@ constexpr bool kValuNT = Q4MV_VALU_NT != 0;
 #ifndef Q4MV_LOWBIT_PREFETCH
 #define Q4MV_LOWBIT_PREFETCH 0
 #endif
+// Output rows per lane group in the paired kernel (2; 4 also gives the same bits).
 #ifndef Q4MV_VALU_PAIR_ROWS
 #define Q4MV_VALU_PAIR_ROWS 2
 #endif
@@ -386,25 +382,6 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
     // activations in registers for the whole kernel when they fit
     uint4 xr[XREG ? CPL : 1][XREG ? NB : 1][4];
     float xsr[XREG ? CPL : 1][XREG ? NB : 1];
-    // Activations straight from device memory into registers (no LDS, no barrier): the
-    // lane's chunks of every activation row, converted to the pair layout.
-    auto load_xreg_direct = [&]() {
-        if constexpr (XREG) {
-            const size_t xrow0 = (x_shared ? 0 : (size_t)m * nb_total) + r0;
-#pragma unroll
-            for (int k = 0; k < CPL; k++) {
-                const int c = j + (k << log2g);
-#pragma unroll
-                for (int r = 0; r < NB; r++) {
-                    const uint2 *xe_r = xe + (xrow0 + r) * words8 + 4 * c;
-                    const uint2 *xo_r = xo + (xrow0 + r) * words8 + 4 * c;
-#pragma unroll
-                    for (int J = 0; J < 4; J++) xr[k][r][J] = make_pairs(xe_r[J], xo_r[J]);
-                    xsr[k][r] = xsum[(xrow0 + r) * C + c] * kTwoM24;
-                }
-            }
-        }
-    };
     auto load_xreg = [&]() {
         if constexpr (XREG) {
 #pragma unroll
@@ -428,7 +405,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
         // load the step's scale block, NSEG..2*NSEG-1 its bias block; both arrays must be
         // 16-byte aligned (a step's block starts at a multiple of 64*ROWS*CPL bytes)
         constexpr bool kPrefetch = BITS == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
-        constexpr int NSEG = (kPrefetch || kValuXDirect || !SBL) ? 0 : valu_sb_segs(ROWS, CPL, true);
+        constexpr int NSEG = (kPrefetch || !SBL) ? 0 : valu_sb_segs(ROWS, CPL, true);
         const bool sbl = NSEG > 0 &&
             ((reinterpret_cast<uintptr_t>(s_m) | reinterpret_cast<uintptr_t>(b_m)) & 15) == 0;
         uint4 *const sbslot =
@@ -580,16 +557,6 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
                         bcb[t][k] = bn[t][k];
                     }
                 if (ws + wstride < wave_steps) load(ws + wstride, cn, sn, bn);
-                compute(ws);
-            }
-        } else if constexpr (XREG && kValuXDirect) {
-            // activations first (few bytes, cache hits after the first wave), then the first
-            // step's weights; no LDS and no barrier
-            load_xreg_direct();
-            if (ws < wave_steps) load(ws, cc, scb, bcb);
-            for (bool first = true; ws < wave_steps; ws += wstride, first = false) {
-                asm volatile("" ::: "memory");
-                if (!first) load(ws, cc, scb, bcb);
                 compute(ws);
             }
         } else {
@@ -769,19 +736,14 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     // would each run several steps
     const bool prefetch = a.bits == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
     const int nseg =
-        kValuXDirect || prefetch || rows != 1 || nbp != 1 || a.bits != 4 ||
+        prefetch || rows != 1 || nbp != 1 || a.bits != 4 ||
                 wave_steps * a.n_mat < (long)Q4MV_VALU_SBLDS_MIN_STEPS * device_cus() * 2 * 4
             ? 0 : valu_sb_segs(rows, cpl, valu_specialised(log2g, cpl, a.bits));
     ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl, false)
                 : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl, false)
                               : pick<4>(rows, nbp, log2g, cpl, nseg > 0);
-    // activations straight into registers need no LDS (same rule as the kernel's XREG; the
-    // generic kernel and NB > 4 always stage)
-    const bool xdirect = kValuXDirect && nbp <= 4 && valu_specialised(log2g, cpl, a.bits) &&
-                         nbp * cpl <= Q4MV_VALU_XREG_MAX;
-    const size_t lds = xdirect ? 0
-                               : (((size_t)nbp * C * 68 + 15) & ~(size_t)15) +
-                                     (size_t)(kValuThreads / 64) * 2 * nseg * 16;
+    const size_t lds = (((size_t)nbp * C * 68 + 15) & ~(size_t)15) +
+                       (size_t)(kValuThreads / 64) * 2 * nseg * 16;
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
     // persistent blocks: enough to fill every CU a few times over, shared by the matrices
