@@ -72,6 +72,10 @@ constexpr bool kValuNT = Q4MV_VALU_NT != 0;
 #ifndef Q4MV_VALU_PAIR_ROWS
 #define Q4MV_VALU_PAIR_ROWS 2
 #endif
+// Code widths whose one-row nb = 1 kernel uses the block-loaded scales (bit b: width b).
+#ifndef Q4MV_VALU_SBLDS_BITS
+#define Q4MV_VALU_SBLDS_BITS ((1 << 4) | (1 << 3) | (1 << 2))
+#endif
 // Scales and biases of a wave step: the step's rows are consecutive, so their scales (and
 // their biases) form one contiguous block; it is read with 16-byte loads (one instruction
 // for both arrays) into a per-wave LDS slot and each lane picks its values from there,
@@ -687,7 +691,8 @@ static ValuFn pick_shape(int log2g, int cpl, bool sbl = false)
 {
 #define Q4MV_PICK(L, K)                                                                   \
     if (log2g == L && cpl == K) {                                                         \
-        if constexpr (NB == 1 && ROWS == 1 && BITS == 4 && valu_sb_segs(1, K, true) > 0)  \
+        if constexpr (NB == 1 && ROWS == 1 && ((Q4MV_VALU_SBLDS_BITS >> BITS) & 1) &&       \
+                      valu_sb_segs(1, K, true) > 0)                                       \
             if (sbl) return valu_kernel<NB, ROWS, L, K, BITS, true>;                      \
         return valu_kernel<NB, ROWS, L, K, BITS>;                                         \
     }
@@ -736,11 +741,11 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     // would each run several steps
     const bool prefetch = a.bits == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
     const int nseg =
-        prefetch || rows != 1 || nbp != 1 || a.bits != 4 ||
+        prefetch || rows != 1 || nbp != 1 || !((Q4MV_VALU_SBLDS_BITS >> a.bits) & 1) ||
                 wave_steps * a.n_mat < (long)Q4MV_VALU_SBLDS_MIN_STEPS * device_cus() * 2 * 4
             ? 0 : valu_sb_segs(rows, cpl, valu_specialised(log2g, cpl, a.bits));
-    ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl, false)
-                : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl, false)
+    ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl, nseg > 0)
+                : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl, nseg > 0)
                               : pick<4>(rows, nbp, log2g, cpl, nseg > 0);
     const size_t lds = (((size_t)nbp * C * 68 + 15) & ~(size_t)15) +
                        (size_t)(kValuThreads / 64) * 2 * nseg * 16;
