@@ -376,6 +376,6 @@ const char *q4mv_status_str(int status)
     }
 }
 
-int q4mv_version(void) { return 300; }
+int q4mv_version(void) { return 400; }
 
 }  // extern "C"
