@@ -158,6 +158,8 @@ class Problem:
         return g
 
     def _time_graph(self, g, n, warmup_replays=1, reps=3):
+        """Median ms per iteration over reps replays of g (n iterations each); the per-replay
+        figures are kept in self.trials."""
         torch = self.torch
         for _ in range(warmup_replays):
             g.replay()
@@ -170,6 +172,7 @@ class Problem:
             b.record()
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b) / n)
+        self.trials = ts
         return statistics.median(ts)
 
     def check_graph_output(self):
@@ -189,15 +192,23 @@ class Problem:
             if not torch.equal(got, two):
                 raise RuntimeError("fused step differs from q4mv_prepare_x + q4mv")
 
-    def time_steps(self, steps, warmup):
+    def time_steps(self, steps, warmup, reps=3):
         """ms per full step (prep + GEMV), graph-captured."""
         def step(i):
             self.prep()
             self.gemv(i)
         g = self._graph(step, steps)
-        ms = self._time_graph(g, steps, warmup_replays=max(1, math.ceil(warmup / steps)))
+        ms = self._time_graph(g, steps, warmup_replays=max(1, math.ceil(warmup / steps)),
+                              reps=reps)
         self.check_graph_output()
         return ms
+
+    def time_prep(self, launches=200):
+        """Average q4mv_prepare_x ms over a graph of back-to-back launches."""
+        q4 = self.q4
+        g = self._graph(lambda i: q4.q4mv_prepare_x(self.x, self.xe, self.xo, self.xsum),
+                        launches)
+        return self._time_graph(g, launches)
 
     def time_kernel(self, launches=200):
         """Average GEMV kernel ms over a graph of back-to-back launches."""
@@ -528,7 +539,8 @@ def main():
         step_ms = prob.time_eager(args.steps, args.warmup)
         kern_ms = step_ms
     else:
-        step_ms = prob.time_steps(args.steps, args.warmup)
+        step_ms = prob.time_steps(args.steps, args.warmup, reps=5)
+        trials = sorted(prob.trials)
         # a fused step is exactly one launch of the GEMV kernel: its timed region is the
         # kernel's (HIP events around the graph of back-to-back launches on the launch stream)
         kern_ms = step_ms if prob.fused else prob.time_kernel(args.steps)
@@ -542,6 +554,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 6),
+        "step_us_min_median_max": None if args.eager else
+        [round(trials[0] * 1e3, 3), round(step_ms * 1e3, 3), round(trials[-1] * 1e3, 3)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -587,6 +601,20 @@ def main():
                           "two_launch_step_us": round(two * 1e3, 3), "path": p.path})
             del p
             torch.cuda.empty_cache()
+        # single weight buffer (no rotation: the 219 MB of weights fit in the 256 MB
+        # Infinity Cache, so this is a cache-resident figure, not an HBM one), and the prep
+        # launch alone
+        p = Problem("lm_head", 1, rotate=False, fused=True)
+        ms = p.time_steps(200, 20)
+        prep_ms = p.time_prep(200)
+        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
+        sweep.append({"workload": "lm_head", "nb": 1, "hot": "single weight buffer, "
+                      "cache-resident", "fused_step_us": round(ms * 1e3, 3),
+                      "weight_GBps": round(gbps, 1)})
+        sweep.append({"workload": "lm_head", "nb": 1, "launch": "q4mv_prepare_x alone",
+                      "prep_us": round(prep_ms * 1e3, 3)})
+        del p
+        torch.cuda.empty_cache()
         # fused epilogues: the silu(y / div) store, and the expert MLP chain
         p = Problem("lm_head", 1, silu_div=2.0)
         ms = p.time_kernel(200)
