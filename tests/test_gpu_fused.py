@@ -159,3 +159,46 @@ def test_moe_layer_fused_equals_five_launches():
     out_f = q4.q4mv_combine(y_f, wmap_d)
     torch.cuda.synchronize()
     assert torch.equal(gu_f, gu) and torch.equal(y_f, y) and torch.equal(out_f, out)
+
+
+def test_fused_graph_replays():
+    """q4mv_fused and the fused expert chain captured in a HIP graph: every replay (with
+    eager work and synchronisations between them, and new inputs copied in) equals the eager
+    result bit for bit."""
+    case = workloads.make_shape(2, 1000, 2560, 4, seed=91)
+    d = upload(case)
+    n_mat, nb = 2, 4
+    y = torch.empty((n_mat, nb, 1000), dtype=torch.float32, device="cuda")
+    sel = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
+    gu = torch.empty((n_mat * nb, 2 * 2560), dtype=torch.float32, device="cuda")
+    ye = torch.empty((2, nb, 1000), dtype=torch.float32, device="cuda")
+    x_in = d["x"].clone()
+    gu_in = torch.randn(n_mat * nb, 2 * 2560, device="cuda")
+
+    def body():
+        q4.q4mv_fused(d["w"], d["s"], d["b"], x_in, nb, y=y)
+        q4.q4mv_experts_fused(d["w"], d["s"], d["b"], sel, gu, nb, False, swiglu=True, y=ye)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gu.copy_(gu_in)
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    rng = np.random.default_rng(5)
+    for rep in range(3):
+        x_in.copy_(torch.from_numpy(rng.standard_normal(tuple(x_in.shape)).astype(np.float32)))
+        gu.copy_(torch.from_numpy(rng.standard_normal(tuple(gu.shape)).astype(np.float32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_y, got_ye = y.clone(), ye.clone()
+        flush(f"[fused graph] replay {rep}")
+        want_y = q4.q4mv_fused(d["w"], d["s"], d["b"], x_in, nb)
+        want_ye = q4.q4mv_experts_fused(d["w"], d["s"], d["b"], sel, gu, nb, False, swiglu=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got_y, want_y) and torch.equal(got_ye, want_ye), f"replay {rep}"
