@@ -287,13 +287,21 @@ int q4mv_lowbit(int bits, const uint32_t *w, const uint16_t *scales, const uint1
     if (!aligned(w, 8) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(scales, 2) ||
         !aligned(biases, 2) || !aligned(xsum, 4) || !aligned(y, 4))
         return Q4MV_ERR_ALIGN;
-    if (path < kAuto || path > kValu2) return Q4MV_ERR_PATH;
-    if (path == kAuto) path = (nb > 1 && out_dim % 2 == 0) ? kValu2 : kValu1;
+    if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
+    // the MFMA kernel takes low-bit codes with 8-wave blocks and 8- or 16-byte scale loads
+    const bool mfma_fits =
+        mfma_shape(in_dim, nb, (long)n_mat * ((out_dim + 31) / 32)).wpb == 8 &&
+        (in_dim / 64) % 4 == 0 && aligned(scales, 8) && aligned(biases, 8);
+    // automatic: the MFMA kernel from nb = 4 where it fits (measured faster there, slower at
+    // nb = 2), else the VALU kernels as q4mv chooses them
+    if (path == kAuto)
+        path = nb > 3 && mfma_fits ? kMfma : (nb > 1 && out_dim % 2 == 0) ? kValu2 : kValu1;
     if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
+    if (path == kMfma && !mfma_fits) return Q4MV_ERR_SHAPE;
     GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb, 0.0f,
                static_cast<hipStream_t>(stream)};
     a.bits = bits;
-    hipError_t e = launch_valu(a, path == kValu2 ? 2 : 1);
+    hipError_t e = path == kMfma ? launch_mfma(a) : launch_valu(a, path == kValu2 ? 2 : 1);
     return e == hipSuccess ? Q4MV_OK : Q4MV_ERR_LAUNCH;
 }
 

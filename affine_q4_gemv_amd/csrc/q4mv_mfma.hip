@@ -94,13 +94,41 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // 2-byte values (compact loads).
 struct SbRegs { uint32_t v[4]; };
 
+// Q2/Q3 codes (the low-bit layouts of the VALU kernels) in the Q4 nibble layout, so the
+// rest of the kernel is unchanged: 2-bit fields at bits 2k and 16 + 2k of t (k < 4) move to
+// nibbles k and 4 + k.
+__device__ __forceinline__ uint32_t spread2(uint32_t t)
+{
+    t = (t | (t << 4)) & 0x0F0F0F0Fu;
+    return (t | (t << 2)) & 0x33333333u;
+}
+
+// One 32-code chunk, {upper word 0, upper word 1, low-bit word (Q3), 0} -> its four Q4 words:
+// Q4 word 2i + u, nibble p is the code of column 32c + 16i + 8u + p, whose 2-bit field (Q2,
+// or Q3's upper two bits) sits in word i at bit (p < 4 ? 0 : 16) + 2(4u + (p & 3)), and
+// whose Q3 lowest bit sits in the low-bit word at bit (p < 4 ? 0 : 16) + 8u + 2(p & 3) + i.
+template <int BITS>
+__device__ __forceinline__ u32x4 lowbit_to_q4(const u32x4 v)
+{
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            uint32_t q = spread2((v[i] >> (8 * u)) & 0x00FF00FFu);
+            if constexpr (BITS == 3) q = (q << 1) | spread2((v[2] >> (8 * u + i)) & 0x00550055u);
+            o[2 * i + u] = q;
+        }
+    return o;
+}
+
 // WPB: waves per block. KS: waves per tile (K-split). NB16: activation rows 8..15 are live
 // (nb > 8). SBW: how a lane loads its row's scales (lanes 0..31) or biases (32..63):
 // 16 = one aligned 16-byte load for two quads, made by the unit of the even quad (or the
 // first unit of a part) and kept in the scratch for the next (groups % 8 == 0, 16-byte
 // aligned arrays; halves the scattered scale loads); 8 = one aligned 8-byte load per quad
 // (groups % 4 == 0, 8-byte aligned); 2 = four 2-byte loads with clamped indices.
-template <int WPB, int KS, bool NB16, int SBW, bool MF16>
+template <int WPB, int KS, bool NB16, int SBW, bool MF16, int BITS = 4>
 __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
@@ -276,6 +304,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
         if (bad) epi_div = __builtin_nanf("");
     }
     const uint4 *const w_m = w + (size_t)e * out_dim * C;
+    // low-bit codes: rows of C * BITS words (Q2: 2 words per chunk; Q3: 2C upper words,
+    // then C low-bit words)
+    const uint32_t *const wl_m =
+        reinterpret_cast<const uint32_t *>(w) + (size_t)e * out_dim * C * BITS;
     const uint16_t *const s_m = scales + (size_t)e * out_dim * groups;
     const uint16_t *const b_m = biases + (size_t)e * out_dim * groups;
     float *const y_m = y + (size_t)m * nb * out_dim;
@@ -291,8 +323,18 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     auto load = [&](int tile, int qd, int u, u32x4 (&cw)[4], SbRegs &sb) {
         const int trow = tile_row(tile);
         const int chunk = min(8 * qd + lc, C - 1);
+        if constexpr (BITS != 4) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
+            for (int r = 0; r < 4; r++) {
+                const int row = narrow ? min(8 * r + lr8, out_dim - 1) : 8 * r + lr8;
+                const uint32_t *wr = wl_m + (size_t)(trow + row) * C * BITS;
+                const u32x2 up = *reinterpret_cast<const u32x2 *>(wr + 2 * chunk);
+                cw[r] = u32x4{up[0], up[1], BITS == 3 ? wr[2 * C + chunk] : 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < (BITS == 4 ? 4 : 0); r++) {
             const int row = narrow ? min(8 * r + lr8, out_dim - 1) : 8 * r + lr8;
 #if Q4MV_MFMA_NT
             // each 128-byte line is read whole, once: non-temporal
@@ -333,7 +375,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = 8 * r + lr8;
-            reinterpret_cast<u32x4 *>(scratch)[row * 8 + (lc ^ (row & 7))] = cw[r];
+            reinterpret_cast<u32x4 *>(scratch)[row * 8 + (lc ^ (row & 7))] =
+                BITS == 4 ? cw[r] : lowbit_to_q4<BITS>(cw[r]);
         }
         if constexpr (SBW == 16) {
             if ((qd & 1) == 0 || u == 0)
@@ -347,6 +390,16 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint4 *const xrow =
         MF16 ? lds + min(n16, nb - 1) * RS + 2 * kb : lds + min(n, nb - 1) * RS + 4 * h;
     float acc[NACC];
+    // Low-bit codes reconstruct at the middle of the 4-bit range each stands for:
+    // w = (4q + 1.5) s + b (Q2), (2q + 0.5) s + b (Q3); the fold takes K s and M s + b (formed
+    // in f32 with one rounding), as the VALU kernels' low-bit fold does.
+    auto midpoint = [](float &s, float &b) {
+        if constexpr (BITS != 4) {
+            constexpr float kq = BITS == 2 ? 4.0f : 2.0f, km = BITS == 2 ? 1.5f : 0.5f;
+            b = __builtin_fmaf(km, s, b);
+            s = kq * s;
+        }
+    };
 
     // The block walks tile steps in lockstep when KS > 1 (one barrier per tile); with
     // KS = 1 each wave stops on its own.
@@ -427,8 +480,9 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                     const uint32_t bwd = (g4 < 2) ? b4[t].x : b4[t].y;
                     const uint32_t sbits = (g4 & 1) ? (sw & 0xFFFF0000u) : (sw << 16);
                     const uint32_t bbits = (g4 & 1) ? (bwd & 0xFFFF0000u) : (bwd << 16);
-                    const float s = __uint_as_float(live ? sbits : 0u);
-                    const float b = __uint_as_float(live ? bbits : 0u);
+                    float s = __uint_as_float(live ? sbits : 0u);
+                    float b = __uint_as_float(live ? bbits : 0u);
+                    midpoint(s, b);
 #pragma unroll
                     for (int v = 0; v < 4; v++)
                         acc[4 * t + v] =
@@ -446,8 +500,9 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                 const uint32_t sw = (g4 < 2) ? s4.x : s4.y, bw = (g4 < 2) ? b4.x : b4.y;
                 const uint32_t sbits = (g4 & 1) ? (sw & 0xFFFF0000u) : (sw << 16);
                 const uint32_t bbits = (g4 & 1) ? (bw & 0xFFFF0000u) : (bw << 16);
-                const float s = __uint_as_float(live ? sbits : 0u);
-                const float b = __uint_as_float(live ? bbits : 0u);
+                float s = __uint_as_float(live ? sbits : 0u);
+                float b = __uint_as_float(live ? bbits : 0u);
+                midpoint(s, b);
                 const uint4 bc = scratch[n * 8 + ((2 * g4 + h) ^ (n & 7))];
                 const int gx = min(g, groups - 1);
                 const uint4 *xg = xrow + 8 * gx;
@@ -531,6 +586,30 @@ static MfmaFn pick_sb(int sbw)
                       : mfma_kernel<WPB, KS, NB16, 2, MF16>;
 }
 
+// Low-bit codes: 8-wave blocks and 8- or 16-byte scale loads only (q4mv_lowbit checks).
+template <int BITS, int KS>
+static MfmaFn pick_lowbit_ks(bool nb16, int sbw, bool mf16)
+{
+    if constexpr (KS <= 2)
+        if (mf16)
+            return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, false, 16, true, BITS>
+                             : mfma_kernel<kMfmaWaves, KS, false, 8, true, BITS>;
+    if (nb16)
+        return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, true, 16, false, BITS>
+                         : mfma_kernel<kMfmaWaves, KS, true, 8, false, BITS>;
+    return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, false, 16, false, BITS>
+                     : mfma_kernel<kMfmaWaves, KS, false, 8, false, BITS>;
+}
+
+template <int BITS>
+static MfmaFn pick_lowbit(int ks, bool nb16, int sbw, bool mf16)
+{
+    return ks == 1   ? pick_lowbit_ks<BITS, 1>(nb16, sbw, mf16)
+           : ks == 2 ? pick_lowbit_ks<BITS, 2>(nb16, sbw, mf16)
+           : ks == 4 ? pick_lowbit_ks<BITS, 4>(nb16, sbw, mf16)
+                     : pick_lowbit_ks<BITS, 8>(nb16, sbw, mf16);
+}
+
 template <int WPB, int KS>
 static MfmaFn pick(bool nb16, int sbw, bool mf16)
 {
@@ -587,7 +666,11 @@ hipError_t launch_mfma(const GemvArgs &a)
         sbw = 16;
     const size_t lds = lds0 + (size_t)sh.wpb * scratch_units(sbw) * 16;
     MfmaFn fn;
-    if (sh.wpb == kMfmaWaves)
+    if (a.bits != 4) {
+        if (sh.wpb != kMfmaWaves || sbw == 2) return hipErrorInvalidValue;  // checked on the host
+        fn = a.bits == 2 ? pick_lowbit<2>(sh.ks, nb16, sbw, mf16)
+                         : pick_lowbit<3>(sh.ks, nb16, sbw, mf16);
+    } else if (sh.wpb == kMfmaWaves)
         fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sbw, mf16)
              : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sbw, mf16)
              : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sbw, mf16)

@@ -221,11 +221,15 @@ int q4mv_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows
  * 32-code chunk acc += K s sum(q x) + (M s + b) sum(x). Same arguments, layouts and
  * accumulation as q4mv except:
  *   bits : 2 or 3;  w : u32 [n_mat][out_dim][in_dim/32*bits] (q4mv_pack_lowbit layout)
- *   path : 0 automatic (1 for nb = 1 or odd out_dim, else 2), 1 one row per lane group,
- *          2 two rows per lane group (out_dim even). The two give bitwise the same result.
- * The matrix-core kernel is not offered for these widths.
- * Errors: as q4mv (w 8-byte aligned), plus VALUE for bits, PATH for a path outside 0..2,
- * ODD_ROWS for path 2 with odd out_dim.
+ *   path : 0 automatic (3 for nb >= 4 where path 3 is accepted; else 1 for nb = 1 or odd
+ *          out_dim, and 2 otherwise), 1 VALU kernel, one row per lane group, 2 VALU kernel,
+ *          two rows per lane group (out_dim even; bitwise the same result as 1), 3 the MFMA
+ *          kernel (the codes moved into the Q4 nibble layout as each tile is staged, the
+ *          tiled product of the page's expert GEMM fn_expert_qmm; needs in_dim/64 a
+ *          multiple of 4, scales and biases 8-byte aligned, and the 8-wave launch shape of
+ *          q4mv_path's path 3).
+ * Errors: as q4mv (w 8-byte aligned), plus VALUE for bits, PATH for a path outside 0..3,
+ * ODD_ROWS for path 2 with odd out_dim, SHAPE for path 3 where it is not accepted.
  */
 int q4mv_lowbit(int bits, const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
                 const void *xe, const void *xo, const float *xsum, float *y, int n_mat,

@@ -204,7 +204,11 @@ def test_lowbit_validation(L):
         for kw in (dict(w=A + 4), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1), dict(xsum=A + 2),
                    dict(y=A + 1)):
             assert f(bits, *gemv_args(**kw), 0, None) == EALIGN, kw
-        assert f(bits, *gemv_args(), 3, None) == EPATH   # no matrix-core kernel
+        # the matrix-core kernel needs in_dim/64 % 4 == 0 and 8-byte aligned scales/biases
+        assert f(bits, *gemv_args(), 3, None) == ESHAPE
+        assert f(bits, *gemv_args(ind=256, s=A + 2), 3, None) == ESHAPE
+        assert f(bits, *gemv_args(ind=256, b=A + 4), 3, None) == ESHAPE
+        assert f(bits, *gemv_args(), 4, None) == EPATH
         assert f(bits, *gemv_args(), -1, None) == EPATH
         assert f(bits, *gemv_args(out=7), 2, None) == EODD
     for bits in (1, 4, 0):

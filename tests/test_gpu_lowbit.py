@@ -1,7 +1,8 @@
 """GPU parity of the Q2 / Q3 low-bit variants (fn_q2_rows_h, fn_q3_rows_h on the Constant
 BATCH_MSL page) through the C ABI: the packed layout bit for bit against the oracle's packer,
-and q4mv_lowbit against the oracle's midpoint-reconstruction GEMV on every VALU path, at the
-workload shapes, ragged shapes, and the full LM head on sampled rows."""
+and q4mv_lowbit against the oracle's midpoint-reconstruction GEMV on every path (the VALU
+kernels, and the MFMA kernel where in_dim/64 is a multiple of 4), at the workload shapes,
+ragged shapes, and the full LM head on sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -22,6 +23,12 @@ def upload_lowbit(case, bits):
     xe, xo, xsum = q4.q4mv_prepare_x(x)
     return dict(w=w, s=bf16_tensor(case["scales"]), b=bf16_tensor(case["biases"]), xe=xe,
                 xo=xo, xsum=xsum, nb=nb)
+
+
+def mfma_ok(in_dim, nb, out_dim):
+    """Whether q4mv_lowbit accepts path 3 for the shape (8-wave MFMA blocks, groups % 4)."""
+    return (in_dim // 64) % 4 == 0 and (nb > 3 or in_dim < 20800) and \
+        q4.q4mv_auto_path(in_dim, max(nb, 4), False, out_dim) == q4.PATH_MFMA
 
 
 def run(d, bits, path):
@@ -58,12 +65,21 @@ def test_lowbit_parity(oracle_lib, bits, name, nb):
         flush(f"[lowbit] bits={bits} {name} nb={nb} path={path}")
         ys[path] = run(d, bits, path)
         parity(ys[path].cpu().numpy(), y_ref, bound, f"Q{bits} {name} nb={nb} path={path}")
-    for path in paths[1:] + [0]:
+    for path in paths[1:]:
         assert torch.equal(ys[path], ys[1]), f"path {path} differs bitwise from path 1"
+    auto_mfma = nb > 3 and mfma_ok(case["in_dim"], nb, case["out_dim"])
+    if mfma_ok(case["in_dim"], nb, case["out_dim"]):
+        flush(f"[lowbit] bits={bits} {name} nb={nb} path=3")
+        ys[3] = run(d, bits, 3)
+        parity(ys[3].cpu().numpy(), y_ref, bound, f"Q{bits} {name} nb={nb} MFMA")
+    # the automatic choice is bitwise the path it takes (MFMA from nb = 4 where it fits)
+    assert torch.equal(ys[0], ys[3] if auto_mfma else ys[1]), "automatic path"
+
 
 
 RAGGED = [(1, 1, 64, 1), (1, 77, 192, 3), (2, 33, 4160, 2), (1, 130, 640, 16),
-          (3, 64, 2560, 5)]
+          (3, 64, 2560, 5), (2, 45, 1024, 7), (1, 1000, 256, 16), (1, 3, 512, 4),
+          (1, 40003, 512, 12)]
 
 
 @pytest.mark.parametrize("bits", [2, 3])
@@ -74,7 +90,10 @@ def test_lowbit_ragged(oracle_lib, bits, n_mat, out_dim, in_dim, nb):
     y_ref, bound = oracle_lib.gemv_lowbit(bits, case["codes"], case["scales"], case["biases"],
                                           case["x"])
     d = upload_lowbit(case, bits)
-    for path in ([1, 2] if out_dim % 2 == 0 else [1]):
+    paths = [1, 2] if out_dim % 2 == 0 else [1]
+    if mfma_ok(in_dim, nb, out_dim):
+        paths.append(3)
+    for path in paths:
         flush(f"[lowbit ragged] bits={bits} {n_mat}x{out_dim}x{in_dim} nb={nb} path={path}")
         parity(run(d, bits, path).cpu().numpy(), y_ref, bound, f"Q{bits} path {path}")
 
@@ -94,3 +113,20 @@ def test_lowbit_lm_head_sampled(oracle_lib, bits):
     y_ref, bound = oracle_lib.gemv_lowbit(bits, case["codes"], case["scales"], case["biases"],
                                           case["x"], rows=rows)
     parity(y[:, :, rows], y_ref, bound, f"Q{bits} lm_head sampled")
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("nb", [4, 16])
+def test_lowbit_lm_head_mfma(oracle_lib, bits, nb):
+    """The full LM head on the MFMA kernel (16x16x32, K-split 2), 768 sampled rows."""
+    case = workloads.make_case("lm_head", nb=nb)
+    out_dim = case["out_dim"]
+    rng = np.random.default_rng(6 + nb)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(out_dim - 128, out_dim),
+                                     rng.integers(0, out_dim, 512)]))
+    flush(f"[lowbit lm_head mfma] bits={bits} nb={nb}")
+    d = upload_lowbit(case, bits)
+    y = run(d, bits, 3).cpu().numpy()
+    y_ref, bound = oracle_lib.gemv_lowbit(bits, case["codes"], case["scales"], case["biases"],
+                                          case["x"], rows=rows)
+    parity(y[:, :, rows], y_ref, bound, f"Q{bits} lm_head nb={nb} MFMA")
