@@ -583,7 +583,8 @@ def main():
     if not args.no_sweep and not args.eager:
         sweep = []
         runs = [("lm_head", nb) for nb in (1, 4, 8, 16)] + [("up", nb) for nb in (1, 4, 8)] + \
-               [("moe_down", 4), ("dense", 1), ("dense", 4), ("dense", 8)]
+               [("moe_down", nb) for nb in (4, 1, 8)] + [("dense", nb) for nb in (1, 4, 8)] + \
+               [("tiny", 1)]  # tiny: launch-bound, its time only (no roofline claim)
         for name, nb in runs:
             # kernel_us: q4mv on prepared activations; fused_step_us: q4mv_fused (prep
             # inside, one launch); two_launch_step_us: q4mv_prepare_x + q4mv
