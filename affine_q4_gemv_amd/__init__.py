@@ -27,7 +27,6 @@ LIB_PATH = os.path.join(HERE, "libq4mv.so")
 Q4MV_OK = 0
 PATH_AUTO, PATH_VALU, PATH_VALU_2ROW, PATH_MFMA = 0, 1, 2, 3
 MAX_NB = 16
-MAX_NB_X_IN = 65536
 
 _lib = None
 

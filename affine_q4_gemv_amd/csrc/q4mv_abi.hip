@@ -8,22 +8,25 @@
 
 namespace q4mv_impl {
 
-// nb up to this value runs on the VALU dot-product kernels, above it on the MFMA kernel
-// (measured crossover on MI355X).
+// nb up to this value runs on the VALU dot-product kernels on short launches, above it on
+// the MFMA kernel; from 2 rows the MFMA kernel already wins on matrices of at least
+// kMfmaMinTilesSmallNb 32-row tiles (measured crossovers on MI355X: LM head NB=2 MFMA 40.5 us
+// against 43.1 two-row and 46.2 one-row; 9728 x 2560 NB=2 one-row 7.8 us against 8.5 MFMA).
 constexpr int kValuAutoMaxNB = 3;
+constexpr long kMfmaMinTilesSmallNb = 1024;
 
-// The automatic choice: MFMA for larger batches when its LDS footprint fits (else the VALU
-// kernels, which handle every nb). Below that, q4mv_2row runs the two-row
-// kernel; q4mv runs one activation row on the one-row kernel (on MI355X it is as fast or
-// faster at every measured shape, the 640-wide expert down projection included) and 2..3
-// rows on the two-row kernel when out_dim is even. The one-row and two-row kernels give
-// bitwise the same result, so q4mv and q4mv_2row agree whichever they take.
+// The automatic choice, from (nb, out_dim) only: MFMA for larger batches (K-sliced where the
+// staged activations of a whole row do not fit in LDS), else one of the VALU kernels:
+// q4mv runs the one-row kernel (on MI355X as fast or faster than the two-row kernel at every
+// measured shape, the 640-wide expert down projection included) and q4mv_2row the two-row
+// kernel. The one-row and two-row kernels give bitwise the same result, so q4mv and q4mv_2row
+// agree whichever they take.
 int auto_path(int in_dim, int nb, bool two_row, int out_dim)
 {
-    // the MFMA kernel's LDS footprint does not depend on the tile count for the fit itself
-    if (nb > kValuAutoMaxNB && mfma_shape(in_dim, nb, 1).wpb != 0) return kMfma;
-    if (two_row) return kValu2;
-    return nb > 1 && out_dim % 2 == 0 ? kValu2 : kValu1;
+    (void)in_dim;
+    const long tiles = (out_dim + 31) / 32;
+    if (nb > kValuAutoMaxNB || (nb > 1 && tiles >= kMfmaMinTilesSmallNb)) return kMfma;
+    return two_row ? kValu2 : kValu1;
 }
 
 int device_cus()
@@ -99,7 +102,7 @@ static int check_weights(const uint32_t *w, const uint16_t *scales, const uint16
 {
     if (!w || !scales || !biases || !y) return Q4MV_ERR_NULL;
     if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
-        nb > Q4MV_MAX_NB || (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        nb > Q4MV_MAX_NB)
         return Q4MV_ERR_SHAPE;
     if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(y, 4))
         return Q4MV_ERR_ALIGN;
@@ -128,7 +131,7 @@ static int run_path(const uint32_t *w, const uint16_t *scales, const uint16_t *b
     if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
     if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
     if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
-    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_mat * ((out_dim + 31) / 32)).wpb == 0)
+    if (path == kMfma && mfma_slice(in_dim, nb, (out_dim + 31) / 32, false) == 0)
         return Q4MV_ERR_SHAPE;
     GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_mat, out_dim, in_dim, nb, epi_div,
                static_cast<hipStream_t>(stream)};
@@ -146,8 +149,7 @@ static int run_experts(const uint32_t *w, const uint16_t *scales, const uint16_t
 {
     if (!w || !scales || !biases || !sel || !y) return Q4MV_ERR_NULL;
     if (n_bank < 1 || n_sel < 1 || n_sel > 65535 || out_dim < 1 || in_dim < 64 ||
-        in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB ||
-        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB)
         return Q4MV_ERR_SHAPE;
     if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(sel, 4) ||
         !aligned(y, 4))
@@ -156,7 +158,7 @@ static int run_experts(const uint32_t *w, const uint16_t *scales, const uint16_t
     if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
     if (path < 0) return path;
     if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
-    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_sel * ((out_dim + 31) / 32)).wpb == 0)
+    if (path == kMfma && mfma_slice(in_dim, nb, (out_dim + 31) / 32, false) == 0)
         return Q4MV_ERR_SHAPE;
     GemvArgs a{w, scales, biases, xe, xo, xsum, y, n_sel, out_dim, in_dim, nb, 0.0f,
                static_cast<hipStream_t>(stream), sel, n_bank, x_shared != 0};
@@ -207,7 +209,7 @@ int q4mv_fused(const uint32_t *w, const uint16_t *scales, const uint16_t *biases
     if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
     if (path == kAuto) path = auto_path(in_dim, nb, false, out_dim);
     if (path == kValu2 && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
-    if (path == kMfma && mfma_shape(in_dim, nb, (long)n_mat * ((out_dim + 31) / 32)).wpb == 0)
+    if (path == kMfma && mfma_slice(in_dim, nb, (out_dim + 31) / 32, false) == 0)
         return Q4MV_ERR_SHAPE;
     GemvArgs a{w, scales, biases, nullptr, nullptr, nullptr, y, n_mat, out_dim, in_dim, nb,
                0.0f, static_cast<hipStream_t>(stream)};
@@ -282,16 +284,15 @@ int q4mv_lowbit(int bits, const uint32_t *w, const uint16_t *scales, const uint1
     if (!w || !scales || !biases || !xe || !xo || !xsum || !y) return Q4MV_ERR_NULL;
     if (bits != 2 && bits != 3) return Q4MV_ERR_VALUE;
     if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
-        nb > Q4MV_MAX_NB || (long long)nb * in_dim > Q4MV_MAX_NB_X_IN)
+        nb > Q4MV_MAX_NB)
         return Q4MV_ERR_SHAPE;
     if (!aligned(w, 8) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(scales, 2) ||
         !aligned(biases, 2) || !aligned(xsum, 4) || !aligned(y, 4))
         return Q4MV_ERR_ALIGN;
     if (path < kAuto || path > kMfma) return Q4MV_ERR_PATH;
     // the MFMA kernel takes low-bit codes with 8-wave blocks and 8- or 16-byte scale loads
-    const bool mfma_fits =
-        mfma_shape(in_dim, nb, (long)n_mat * ((out_dim + 31) / 32)).wpb == 8 &&
-        (in_dim / 64) % 4 == 0 && aligned(scales, 8) && aligned(biases, 8);
+    const bool mfma_fits = (in_dim / 64) % 4 == 0 && aligned(scales, 8) && aligned(biases, 8) &&
+                           mfma_slice(in_dim, nb, (out_dim + 31) / 32, true) != 0;
     // automatic: the MFMA kernel from nb = 4 where it fits (measured faster there, slower at
     // nb = 2), else the VALU kernels as q4mv chooses them
     if (path == kAuto)
@@ -362,8 +363,7 @@ int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
 
 int q4mv_auto_path(int in_dim, int nb, int two_row, int out_dim)
 {
-    if (in_dim < 64 || in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB ||
-        (long long)nb * in_dim > Q4MV_MAX_NB_X_IN || out_dim < 1)
+    if (in_dim < 64 || in_dim % 64 != 0 || nb < 1 || nb > Q4MV_MAX_NB || out_dim < 1)
         return Q4MV_ERR_SHAPE;
     if (two_row && (out_dim & 1)) return Q4MV_ERR_ODD_ROWS;
     return auto_path(in_dim, nb, two_row != 0, out_dim);
@@ -384,6 +384,6 @@ const char *q4mv_status_str(int status)
     }
 }
 
-int q4mv_version(void) { return 400; }
+int q4mv_version(void) { return 500; }
 
 }  // extern "C"

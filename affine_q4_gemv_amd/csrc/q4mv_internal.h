@@ -83,6 +83,13 @@ inline size_t mfma_part_bytes(int wpb, int ks, int nacc, int lanes)
 // the shape's LDS does not fit in one compute unit.
 struct MfmaShape { int wpb, ks; };
 MfmaShape mfma_shape(int in_dim, int nb, long tiles);
+// Columns per K slice of the MFMA kernel for a row of in_dim: in_dim when the staged
+// activations of the whole row fit in LDS, else the length of the fewest equal slices that
+// fit (8-wave blocks when need8); 0 if none does.
+int mfma_slice(int in_dim, int nb, long tiles, bool need8);
+// Columns per K slice of a VALU launch over nbp activation rows (same rule: in_dim when the
+// whole row's staged activations fit in LDS).
+int valu_slice(int in_dim, int nbp);
 // Raise a kernel's dynamic LDS limit above the 64 KB default (once per kernel and size).
 hipError_t ensure_lds(const void *fn, size_t bytes);
 // Blocks of `fn` that can be resident on one CU at this block size and LDS (cached).

@@ -57,8 +57,7 @@
 #define Q4MV_MFMA_BALANCE 0
 #endif
 // The KS waves of a tile take interleaved quads (wave q: q, q+KS, ...) instead of
-// contiguous ranges when the scale loads are not paired (measured faster for small tile
-// counts).
+// contiguous ranges when the K-split is above 2 (measured faster for small tile counts).
 #ifndef Q4MV_MFMA_INTERLEAVE
 #define Q4MV_MFMA_INTERLEAVE 1
 #endif
@@ -134,16 +133,21 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
     int out_dim, int in_dim, int nb, float epi_div, const int *__restrict__ sel,
-    int n_bank, int x_shared, const float *__restrict__ xf, int xf_glu)
+    int n_bank, int x_shared, const float *__restrict__ xf, int xf_glu, int in_full, int k0,
+    int accum)
 {
     constexpr int TH = WPB * 64;
     constexpr int TPB = WPB / KS;  // tile groups per block
     constexpr int NACC = (MF16 || NB16) ? 8 : 4;
     extern __shared__ uint4 lds[];
     const int m = blockIdx.y;
+    // K slice: columns k0 .. k0+in_dim-1 of rows of in_full columns (in_dim == in_full and
+    // k0 == 0 unless the staged activations of the whole row do not fit in LDS); C, groups,
+    // quads and the staged layout are the slice's, row strides the full row's
     const int C = in_dim >> 5;
     const int groups = in_dim >> 6;
-    const int words8 = in_dim >> 3;
+    const int Cf = in_full >> 5, gf = in_full >> 6, kc0 = k0 >> 5, g0 = k0 >> 6;
+    const int words8 = in_full >> 3;
     const int quads = (groups + 3) >> 2;
 
     // LDS: activations | group sums xsg[g][16] * 2^-24 | partial sums | per-wave scratch.
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // silu(gate) * up (as q4mv_swiglu_prep forms them).
     auto fstage = [&]() {
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
-        const int rs4 = xf_glu ? in_dim >> 1 : in_dim >> 2;  // float4 per row
+        const int rs4 = xf_glu ? in_full >> 1 : in_full >> 2;  // float4 per row
         const float4 *xf_m = reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4;
         const int wrow = in_dim >> 3, words = nb * wrow;
         float *xsw = reinterpret_cast<float *>(xsg_w);
@@ -185,7 +189,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
             for (int i = 0; i < 2; i++) {
                 const int wi = min(base + i * TH, words - 1);
                 const int r = wi / wrow;
-                xword_load(xf_m + (size_t)r * rs4, wi - r * wrow, in_dim, xf_glu, v[i]);
+                xword_load(xf_m + (size_t)r * rs4, (k0 >> 3) + wi - r * wrow, in_full, xf_glu,
+                           v[i]);
             }
 #pragma unroll
             for (int i = 0; i < 2; i++) {
@@ -225,9 +230,9 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
             return;
         }
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
-        const uint2 *xe_m = xe + xrow0 * words8;
-        const uint2 *xo_m = xo + xrow0 * words8;
-        const float *xsum_m = xsum + xrow0 * C;
+        const uint2 *xe_m = xe + xrow0 * words8 + (k0 >> 3);
+        const uint2 *xo_m = xo + xrow0 * words8 + (k0 >> 3);
+        const float *xsum_m = xsum + xrow0 * Cf + kc0;
         const int units = nb * C * 4;  // one per (row, chunk, word)
         const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
         // each round issues all of its loads before any LDS write: one memory round trip
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
         for (int u = threadIdx.x; u < groups * 16; u += TH) {
             const int g = u >> 4, r = u & 15;
             const int rr = min(r, nb - 1);
-            const float a = xsum_m[(size_t)rr * C + 2 * g], b = xsum_m[(size_t)rr * C + 2 * g + 1];
+            const float a = xsum_m[(size_t)rr * Cf + 2 * g], b = xsum_m[(size_t)rr * Cf + 2 * g + 1];
             xsw[u] = r < nb ? (a + b) * kTwoM24 : 0.0f;
         }
         __syncthreads();
@@ -281,8 +286,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // largest part, so it is the same for every wave of the block and every wave meets the
     // per-tile barrier equally often (units past a wave's part are computed with zero
     // scales and biases)
-    // (16-byte scale loads pair consecutive quads, so they keep contiguous parts)
-    constexpr bool kInterleave = Q4MV_MFMA_INTERLEAVE && SBW != 16;
+    // (16-byte scale loads pair consecutive quads, so K-splits of 2 or less, where those
+    // loads apply, keep contiguous parts whatever the scale load width: the summation order
+    // then does not depend on the alignment of the scale arrays)
+    constexpr bool kInterleave = Q4MV_MFMA_INTERLEAVE && KS > 2;
     const int q_begin = kInterleave ? quarter : quarter * quads / KS;
     const int q_step = kInterleave ? KS : 1;
     const int q_end = kInterleave ? quads : (quarter + 1) * quads / KS;
@@ -291,8 +298,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     const int tstride = gridDim.x * TPB;
 
     // Rows: a tile covers rows rb .. rb+31 where the last tile is shifted back to end at
-    // out_dim (its overlap with the previous tile is recomputed with identical arithmetic
-    // and stored again with the same bits). Only when out_dim < 32 are rows clamped.
+    // out_dim (its overlap with the previous tile is recomputed but not stored: every output
+    // is stored once, by the tile it belongs to). Only when out_dim < 32 are rows clamped.
     const bool narrow = out_dim < 32;
     // Weights: matrix m, or bank matrix sel[m]. An id outside the bank reads matrix 0 and
     // stores NaN (a NaN divisor makes the epilogue return NaN).
@@ -303,13 +310,13 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
         e = bad ? 0 : id;
         if (bad) epi_div = __builtin_nanf("");
     }
-    const uint4 *const w_m = w + (size_t)e * out_dim * C;
+    const uint4 *const w_m = w + (size_t)e * out_dim * Cf;
     // low-bit codes: rows of C * BITS words (Q2: 2 words per chunk; Q3: 2C upper words,
     // then C low-bit words)
     const uint32_t *const wl_m =
-        reinterpret_cast<const uint32_t *>(w) + (size_t)e * out_dim * C * BITS;
-    const uint16_t *const s_m = scales + (size_t)e * out_dim * groups;
-    const uint16_t *const b_m = biases + (size_t)e * out_dim * groups;
+        reinterpret_cast<const uint32_t *>(w) + (size_t)e * out_dim * Cf * BITS;
+    const uint16_t *const s_m = scales + (size_t)e * out_dim * gf + g0;
+    const uint16_t *const b_m = biases + (size_t)e * out_dim * gf + g0;
     float *const y_m = y + (size_t)m * nb * out_dim;
     auto tile_row = [&](int tile) { return narrow ? 0 : min(tile * 32, out_dim - 32); };
 
@@ -328,9 +335,9 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int row = narrow ? min(8 * r + lr8, out_dim - 1) : 8 * r + lr8;
-                const uint32_t *wr = wl_m + (size_t)(trow + row) * C * BITS;
-                const u32x2 up = *reinterpret_cast<const u32x2 *>(wr + 2 * chunk);
-                cw[r] = u32x4{up[0], up[1], BITS == 3 ? wr[2 * C + chunk] : 0u, 0u};
+                const uint32_t *wr = wl_m + (size_t)(trow + row) * Cf * BITS;
+                const u32x2 up = *reinterpret_cast<const u32x2 *>(wr + 2 * (kc0 + chunk));
+                cw[r] = u32x4{up[0], up[1], BITS == 3 ? wr[2 * Cf + kc0 + chunk] : 0u, 0u};
             }
         }
 #pragma unroll
@@ -339,12 +346,12 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 #if Q4MV_MFMA_NT
             // each 128-byte line is read whole, once: non-temporal
             cw[r] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(w_m) + (size_t)(trow + row) * C + chunk);
+                reinterpret_cast<const u32x4 *>(w_m) + (size_t)(trow + row) * Cf + kc0 + chunk);
 #else
-            cw[r] = reinterpret_cast<const u32x4 *>(w_m)[(size_t)(trow + row) * C + chunk];
+            cw[r] = reinterpret_cast<const u32x4 *>(w_m)[(size_t)(trow + row) * Cf + kc0 + chunk];
 #endif
         }
-        const uint16_t *srow = sb_m + (size_t)(trow + sbrow) * groups;
+        const uint16_t *srow = sb_m + (size_t)(trow + sbrow) * gf;
         if constexpr (SBW == 16) {
             // only units that start a pair load (measured faster than a dummy load)
             if ((qd & 1) == 0 || u == 0) {
@@ -556,8 +563,14 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                     // row 8(i/4) + 4h + i%4
                     const int orow = tile_row(tile) + (MF16 ? 16 * (i / 4) + n16 : n);
                     const int r = MF16 ? 4 * kb + (i % 4) : 8 * (i / 4) + 4 * h + (i % 4);
-                    if (tile < tiles && orow < out_dim && r < nb)
-                        y_m[(size_t)r * out_dim + orow] = gemv_epilogue(acc[i] * kTwo24, epi_div);
+                    // the shifted last tile stores only rows that no earlier tile stores
+                    if (tile < tiles && orow >= tile * 32 && orow < out_dim && r < nb) {
+                        float v = acc[i] * kTwo24;
+                        // K slices after the first add to what the earlier slices stored;
+                        // only the last slice has a nonzero epi_div
+                        if (accum) v += y_m[(size_t)r * out_dim + orow];
+                        y_m[(size_t)r * out_dim + orow] = gemv_epilogue(v, epi_div);
+                    }
                 }
             }
             step++;
@@ -571,7 +584,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 
 typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, float,
-                       const int *, int, int, const float *, int);
+                       const int *, int, int, const float *, int, int, int, int);
 
 static bool use_mf16(int ks, int nb, long tiles)
 {
@@ -647,21 +660,49 @@ MfmaShape mfma_shape(int in_dim, int nb, long tiles)
     return {0, 0};
 }
 
-hipError_t launch_mfma(const GemvArgs &a)
+// Alignment of K-slice boundaries (columns): whole 8-group (16-byte scale load) or 4-group
+// (8-byte) blocks where the row length allows.
+static int mfma_slice_align(int in_dim)
 {
-    const int groups = a.in_dim / 64;
+    return in_dim % 512 == 0 ? 512 : in_dim % 256 == 0 ? 256 : 64;
+}
+
+int mfma_slice(int in_dim, int nb, long tiles, bool need8)
+{
+    auto ok = [&](int len) {
+        const MfmaShape sh = mfma_shape(len, nb, tiles);
+        return sh.wpb != 0 && (!need8 || sh.wpb == kMfmaWaves);
+    };
+    if (ok(in_dim)) return in_dim;
+    // the fewest equal slices (the last one shorter) whose staged activations fit
+    const int al = mfma_slice_align(in_dim);
+    for (int ns = 2;; ns++) {
+        const int len = ((in_dim + ns - 1) / ns + al - 1) / al * al;
+        if (ok(len)) return len;
+        if (len <= al) return 0;
+    }
+}
+
+// One launch over columns k0 .. k0+klen-1 (the whole row when klen == a.in_dim); accum: add
+// to y instead of overwriting it; epi_div: the epilogue (0: none).
+static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int accum, float epi_div)
+{
+    const int groups = klen / 64, gf = a.in_dim / 64, g0 = k0 / 64;
     const bool nb16 = a.nb > 8;
     const long tiles = (a.out_dim + 31) / 32;
-    const MfmaShape sh = mfma_shape(a.in_dim, a.nb, tiles * a.n_mat);
+    // every choice that changes the arithmetic (K-split, matrix-core shape) comes from one
+    // matrix's tile count, so a matrix gives the same bits alone, batched or as an expert slot
+    const MfmaShape sh = mfma_shape(klen, a.nb, tiles);
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
-    const bool mf16 = use_mf16(sh.ks, a.nb, tiles * a.n_mat);
-    const size_t lds0 =
-        mfma_lds_bytes(a.in_dim, a.nb) + part_bytes(sh.wpb, sh.ks, a.nb, tiles * a.n_mat);
-    // 16-byte scale loads when the layout allows and their larger scratch still fits
-    int sbw = groups % 4 == 0 && (uintptr_t)a.scales % 8 == 0 && (uintptr_t)a.biases % 8 == 0
+    const bool mf16 = use_mf16(sh.ks, a.nb, tiles);
+    const size_t lds0 = mfma_lds_bytes(klen, a.nb) + part_bytes(sh.wpb, sh.ks, a.nb, tiles);
+    // 16-byte scale loads when the layout allows and their larger scratch still fits (every
+    // row's slice of scales must start on an 8- or 16-byte boundary)
+    int sbw = groups % 4 == 0 && gf % 4 == 0 && g0 % 4 == 0 && (uintptr_t)a.scales % 8 == 0 &&
+                      (uintptr_t)a.biases % 8 == 0
                   ? 8 : 2;
-    if (Q4MV_MFMA_SB16 && sh.ks <= Q4MV_MFMA_SB16_MAX_KS && groups % 8 == 0 &&
-        (uintptr_t)a.scales % 16 == 0 && (uintptr_t)a.biases % 16 == 0 &&
+    if (Q4MV_MFMA_SB16 && sh.ks <= Q4MV_MFMA_SB16_MAX_KS && groups % 8 == 0 && gf % 8 == 0 &&
+        g0 % 8 == 0 && (uintptr_t)a.scales % 16 == 0 && (uintptr_t)a.biases % 16 == 0 &&
         lds0 + (size_t)sh.wpb * scratch_units(16) * 16 <= kMaxLds)
         sbw = 16;
     const size_t lds = lds0 + (size_t)sh.wpb * scratch_units(sbw) * 16;
@@ -696,9 +737,25 @@ hipError_t launch_mfma(const GemvArgs &a)
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(sh.wpb * 64), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
-                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, a.epi_div, a.sel, a.n_bank, a.x_shared,
-                       a.xf, a.xf_glu);
+                       a.xsum, a.y, a.out_dim, klen, a.nb, epi_div, a.sel, a.n_bank,
+                       a.x_shared, a.xf, a.xf_glu, a.in_dim, k0, accum);
     return hipGetLastError();
+}
+
+hipError_t launch_mfma(const GemvArgs &a)
+{
+    // rows whose staged activations do not fit in LDS run as K slices, one launch each, in
+    // column order: each later slice adds its partial product to y, and the epilogue comes
+    // with the last
+    const int klen = mfma_slice(a.in_dim, a.nb, (a.out_dim + 31) / 32, a.bits != 4);
+    if (klen == 0) return hipErrorInvalidValue;  // rejected on the host before this point
+    for (int k0 = 0; k0 < a.in_dim; k0 += klen) {
+        const int len = std::min(klen, a.in_dim - k0);
+        const bool last = k0 + len == a.in_dim;
+        const hipError_t e = launch_mfma_slice(a, k0, len, k0 > 0, last ? a.epi_div : 0.0f);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace q4mv_impl

@@ -236,23 +236,27 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
     int out_dim, int in_dim, int nb_total, int r0, int log2g_rt, int cpl_rt, float epi_div,
     const int *__restrict__ sel, int n_bank, int x_shared, const float *__restrict__ xf,
-    int xf_glu)
+    int xf_glu, int in_full, int k0, int accum)
 {
     const int log2g = LOG2G >= 0 ? LOG2G : log2g_rt;
     extern __shared__ uint4 lds[];
     constexpr bool XREG = CPL > 0 && NB * CPL <= Q4MV_VALU_XREG_MAX;
     const int m = blockIdx.y;
+    // K slice: columns k0 .. k0+in_dim-1 of rows of in_full columns (in_dim == in_full and
+    // k0 == 0 unless the activations of the whole row do not fit in LDS); C, groups and the
+    // staged layout are the slice's, row strides the full row's
     const int C = in_dim >> 5;
     const int groups = in_dim >> 6;
-    const int words8 = in_dim >> 3;  // uint2 units (4 halves) per activation row
+    const int Cf = in_full >> 5, gf = in_full >> 6, kc0 = k0 >> 5, g0 = k0 >> 6;
+    const int words8 = in_full >> 3;  // uint2 units (4 halves) per activation row
 
     // Stage activation rows r0 .. r0+NB-1 of matrix m (pair layout + scaled sums) in LDS.
     // stage_load issues one round of loads into registers and stage_store writes them, so a
     // wave can put its first weight loads between the two and the latencies overlap.
     const size_t xrow0 = (x_shared ? 0 : (size_t)m * nb_total) + r0;
-    const uint2 *xe_m = xe + xrow0 * words8;
-    const uint2 *xo_m = xo + xrow0 * words8;
-    const float *xsum_m = xsum + xrow0 * C;
+    const uint2 *xe_m = xe + xrow0 * words8 + (k0 >> 3);
+    const uint2 *xo_m = xo + xrow0 * words8 + (k0 >> 3);
+    const float *xsum_m = xsum + xrow0 * Cf + kc0;
     float *xsw = reinterpret_cast<float *>(lds + NB * C * 4);
     const int units = NB * C * 4;  // 16-byte pair units; NB*C chunk sums
     struct XStage { uint2 e[4], o[4]; float sv; };
@@ -265,8 +269,9 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
             st.e[i] = xe_m[(size_t)r * words8 + cj];
             st.o[i] = xo_m[(size_t)r * words8 + cj];
         }
-        const int us = (base - threadIdx.x) / 4 + threadIdx.x;  // chunk-sum index
-        st.sv = xsum_m[min(us, NB * C - 1)];
+        const int us = min((base - threadIdx.x) / 4 + (int)threadIdx.x, NB * C - 1);  // chunk sum
+        const int rs = us / C;
+        st.sv = xsum_m[(size_t)rs * Cf + (us - rs * C)];
     };
     auto stage_store = [&](int base, const XStage &st) {
 #pragma unroll
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
     // With xf_glu the rows are [gate | up] and the values silu(gate) * up (as
     // q4mv_swiglu_prep forms them).
     const int wrow = in_dim >> 3, words = NB * wrow;
-    const int rs4 = xf_glu ? in_dim >> 1 : in_dim >> 2;  // float4 per row
+    const int rs4 = xf_glu ? in_full >> 1 : in_full >> 2;  // float4 per row
     const float4 *xf_m = xf ? reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4 : nullptr;
     struct FStage { float4 v[2][4]; };
     auto fstage_load = [&](int base, FStage &st) {
@@ -307,7 +312,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
         for (int i = 0; i < 2; i++) {
             const int wi = min(base + i * kValuThreads, words - 1);
             const int r = wi / wrow;
-            xword_load(xf_m + (size_t)r * rs4, wi - r * wrow, in_dim, xf_glu, st.v[i]);
+            xword_load(xf_m + (size_t)r * rs4, (k0 >> 3) + wi - r * wrow, in_full, xf_glu, st.v[i]);
         }
     };
     auto fstage_store = [&](int base, const FStage &st) {
@@ -378,10 +383,16 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
         e = bad ? 0 : id;
         if (bad) epi_div = __builtin_nanf("");
     }
-    const uint32_t *w_m = reinterpret_cast<const uint32_t *>(w) + (size_t)e * out_dim * C * BITS;
-    const uint16_t *s_m = scales + (size_t)e * out_dim * groups;
-    const uint16_t *b_m = biases + (size_t)e * out_dim * groups;
+    const uint32_t *w_m = reinterpret_cast<const uint32_t *>(w) + (size_t)e * out_dim * Cf * BITS;
+    const uint16_t *s_m = scales + (size_t)e * out_dim * gf;
+    const uint16_t *b_m = biases + (size_t)e * out_dim * gf;
     float *y_m = y + ((size_t)m * nb_total + r0) * out_dim;
+    // stored value: the product (plus what y holds from the previous K slices), then the
+    // epilogue; only the last slice of a sliced product has a nonzero epi_div
+    auto out_value = [&](float v, size_t at) {
+        if (accum) v += y_m[at];
+        return gemv_epilogue(v, epi_div);
+    };
 
     // activations in registers for the whole kernel when they fit
     uint4 xr[XREG ? CPL : 1][XREG ? NB : 1][4];
@@ -410,7 +421,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
         // 16-byte aligned (a step's block starts at a multiple of 64*ROWS*CPL bytes)
         constexpr bool kPrefetch = BITS == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
         constexpr int NSEG = (kPrefetch || !SBL) ? 0 : valu_sb_segs(ROWS, CPL, true);
-        const bool sbl = NSEG > 0 &&
+        const bool sbl = NSEG > 0 && in_full == in_dim &&
             ((reinterpret_cast<uintptr_t>(s_m) | reinterpret_cast<uintptr_t>(b_m)) & 15) == 0;
         uint4 *const sbslot =
             reinterpret_cast<uint4 *>(reinterpret_cast<char *>(lds) +
@@ -428,9 +439,9 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
 #pragma unroll
             for (int t = 0; t < ROWS; t++) {
                 const int row = min(ws * rows_per_wave + grp * ROWS + t, out_dim - 1);
-                wr[t] = w_m + (size_t)row * C * BITS;
-                sr[t] = s_m + (size_t)row * groups;
-                br[t] = b_m + (size_t)row * groups;
+                wr[t] = w_m + (size_t)row * Cf * BITS;
+                sr[t] = s_m + (size_t)row * gf + g0;
+                br[t] = b_m + (size_t)row * gf + g0;
             }
             if (sbl) {
                 // segment L of the step's scale (L < NSEG) or bias block; the last step's
@@ -460,7 +471,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
                 const int c = j + (k << log2g);
 #pragma unroll
                 for (int t = 0; t < ROWS; t++) {
-                    cw[t][k] = load_chunk<BITS, kValuNT>(wr[t], c, C);
+                    cw[t][k] = load_chunk<BITS, kValuNT>(wr[t], kc0 + c, Cf);
                     if (sbl) continue;
 #if Q4MV_VALU_NT
                     // streamed once: non-temporal loads (no reuse to keep in the caches)
@@ -537,7 +548,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
 #pragma unroll
                         for (int r = 0; r < NB; r++)
                             y_m[(size_t)r * out_dim + row] =
-                                gemv_epilogue(acc[t][r] * kTwo24, epi_div);
+                                out_value(acc[t][r] * kTwo24, (size_t)r * out_dim + row);
                     }
                 }
             }
@@ -615,9 +626,9 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
                     for (int kk = 0; kk < 4; kk++) {
                         // clamped, unconditional loads (chunks past cpl are never used)
                         const int c = j + (min(k0 + kk, cpl - 1) << log2g);
-                        cc[t][kk] = load_chunk<BITS, false>(w_m + (size_t)rowc[t] * C * BITS, c, C);
-                        sc[t][kk] = s_m[(size_t)rowc[t] * groups + (c >> 1)];
-                        bc[t][kk] = b_m[(size_t)rowc[t] * groups + (c >> 1)];
+                        cc[t][kk] = load_chunk<BITS, false>(w_m + (size_t)rowc[t] * Cf * BITS, kc0 + c, Cf);
+                        sc[t][kk] = s_m[(size_t)rowc[t] * gf + g0 + (c >> 1)];
+                        bc[t][kk] = b_m[(size_t)rowc[t] * gf + g0 + (c >> 1)];
                     }
 #pragma unroll
                 for (int kk = 0; kk < 4; kk++) {
@@ -646,7 +657,8 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
                 for (int r = 0; r < NB; r++) {
                     const float v = group_sum(acc[t][r], log2g);
                     if (j == 0 && row < out_dim)
-                        y_m[(size_t)r * out_dim + row] = gemv_epilogue(v * kTwo24, epi_div);
+                        y_m[(size_t)r * out_dim + row] =
+                            out_value(v * kTwo24, (size_t)r * out_dim + row);
                 }
             }
         }
@@ -658,7 +670,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
 
 typedef void (*ValuFn)(const uint4 *, const uint16_t *, const uint16_t *, const uint2 *,
                        const uint2 *, const float *, float *, int, int, int, int, int, int,
-                       float, const int *, int, int, const float *, int);
+                       float, const int *, int, int, const float *, int, int, int, int);
 
 // (log2 G, CPL) of the specialised row lengths: in_dim = 32 * CPL << log2G.
 #define Q4MV_VALU_SHAPES(X)                                                                   \
@@ -728,30 +740,43 @@ static ValuFn pick(int rows, int nb, int log2g, int cpl, bool sbl)
                      : pick_nb<Q4MV_VALU_PAIR_ROWS, BITS>(nb, log2g, cpl, false);
 }
 
-static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
+// LDS of a VALU launch: nbp staged rows of C chunks (64 bytes of pairs and a 4-byte sum per
+// chunk), then the per-wave scale/bias slots (nseg 16-byte segments per array).
+static size_t valu_lds(int nbp, int C, int nseg)
 {
-    const int log2g = valu_log2g(a.in_dim);
-    const int C = a.in_dim / 32;
+    return (((size_t)nbp * C * 68 + 15) & ~(size_t)15) + (size_t)(kValuThreads / 64) * 2 * nseg * 16;
+}
+
+// One launch over activation rows r0 .. r0+nbp-1 and columns k0 .. k0+klen-1 (the whole row
+// when klen == a.in_dim); accum: add to y instead of overwriting it; epi_div: the epilogue.
+static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp, int k0, int klen,
+                                   int accum, float epi_div)
+{
+    const int log2g = valu_log2g(klen);
+    const int C = klen / 32;
     const int cpl = C >> log2g;
     if (rows == 2) rows = Q4MV_VALU_PAIR_ROWS;
     const int rows_per_wave = (64 >> log2g) * rows;
     const long wave_steps = (a.out_dim + rows_per_wave - 1) / rows_per_wave;
     const long blocks_needed = (wave_steps + 3) / 4;
-    // block-loaded scales (one-row kernel, nb = 1, Q4) when the waves of two blocks per CU
-    // would each run several steps
+    // block-loaded scales (one-row kernel, nb = 1, whole rows) when the waves of two blocks
+    // per CU would each run several steps
     const bool prefetch = a.bits == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
     const int nseg =
-        prefetch || rows != 1 || nbp != 1 || !((Q4MV_VALU_SBLDS_BITS >> a.bits) & 1) ||
+        prefetch || rows != 1 || nbp != 1 || klen != a.in_dim ||
+                !((Q4MV_VALU_SBLDS_BITS >> a.bits) & 1) ||
                 wave_steps * a.n_mat < (long)Q4MV_VALU_SBLDS_MIN_STEPS * device_cus() * 2 * 4
             ? 0 : valu_sb_segs(rows, cpl, valu_specialised(log2g, cpl, a.bits));
     ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl, nseg > 0)
                 : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl, nseg > 0)
                               : pick<4>(rows, nbp, log2g, cpl, nseg > 0);
-    const size_t lds = (((size_t)nbp * C * 68 + 15) & ~(size_t)15) +
-                       (size_t)(kValuThreads / 64) * 2 * nseg * 16;
+    const size_t lds = valu_lds(nbp, C, nseg);
+    if (lds > kMaxLds) return hipErrorInvalidValue;  // the slice length keeps it inside
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
     // persistent blocks: enough to fill every CU a few times over, shared by the matrices
+    // (one round of blocks sized to the row steps, so that no wave runs a second step, was
+    // measured slower on the 9728 x 2560 projection: 6.65 against 5.97 us)
     const long per_cu = std::min<long>(rows != 1      ? Q4MV_VALU_BLOCKS_PER_CU
                                        : a.bits == 4 ? Q4MV_VALU1_BLOCKS_PER_CU
                                                      : Q4MV_LOWBIT1_BLOCKS_PER_CU,
@@ -768,17 +793,41 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp)
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)a.n_mat), dim3(kValuThreads), lds,
                        a.stream, reinterpret_cast<const uint4 *>(a.w), a.scales, a.biases,
                        static_cast<const uint2 *>(a.xe), static_cast<const uint2 *>(a.xo),
-                       a.xsum, a.y, a.out_dim, a.in_dim, a.nb, r0, log2g, cpl, a.epi_div,
-                       a.sel, a.n_bank, a.x_shared, a.xf, a.xf_glu);
+                       a.xsum, a.y, a.out_dim, klen, a.nb, r0, log2g, cpl, epi_div,
+                       a.sel, a.n_bank, a.x_shared, a.xf, a.xf_glu, a.in_dim, k0, accum);
     return hipGetLastError();
+}
+
+int valu_slice(int in_dim, int nbp)
+{
+    // the largest per-wave scale/bias slot (one-row nb = 1 launches) comes on top
+    const size_t slot = (size_t)(kValuThreads / 64) * 2 * valu_sb_segs(1, 8, true) * 16;
+    auto ok = [&](int len) { return valu_lds(nbp, len / 32, 0) + slot <= kMaxLds; };
+    if (ok(in_dim)) return in_dim;
+    // the fewest equal slices (the last one shorter) whose staged activations fit
+    for (int ns = 2;; ns++) {
+        const int len = ((in_dim + ns - 1) / ns + 63) / 64 * 64;
+        if (ok(len)) return len;
+        if (len <= 64) return 0;
+    }
 }
 
 hipError_t launch_valu(const GemvArgs &a, int rows)
 {
+    // batches above kValuMaxNB rows run as launches over row ranges; rows whose staged
+    // activations do not fit in LDS run as K slices, one launch each, in column order: each
+    // later slice adds its partial product to y, and the epilogue comes with the last
     for (int r0 = 0; r0 < a.nb; r0 += kValuMaxNB) {
         const int nbp = std::min(kValuMaxNB, a.nb - r0);
-        hipError_t e = launch_valu_part(a, rows, r0, nbp);
-        if (e != hipSuccess) return e;
+        const int klen = valu_slice(a.in_dim, nbp);
+        if (klen == 0) return hipErrorInvalidValue;
+        for (int k0 = 0; k0 < a.in_dim; k0 += klen) {
+            const int len = std::min(klen, a.in_dim - k0);
+            const bool last = k0 + len == a.in_dim;
+            hipError_t e =
+                launch_valu_part(a, rows, r0, nbp, k0, len, k0 > 0, last ? a.epi_div : 0.0f);
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

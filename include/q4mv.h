@@ -43,9 +43,6 @@ enum {
 
 /* Largest activation batch accepted (rows per matrix). */
 #define Q4MV_MAX_NB 16
-/* nb * in_dim must not exceed this: the activations of one matrix are staged in LDS as
-   f16 (2 bytes each), and one staging must fit in the 160 KB of a gfx950 compute unit. */
-#define Q4MV_MAX_NB_X_IN 65536
 
 /*
  * q4mv_pack_codes -- pack 4-bit codes eight per u32 word, low nibble first.
@@ -108,11 +105,20 @@ int q4mv_prepare_x(const float *x, int n_rows, int in_dim, void *xe, void *xo, f
  *   y       : f32 [n_mat][nb][out_dim]          fully overwritten, nothing written beyond
  * Matrix m reads activation rows m*nb .. m*nb+nb-1 (the expert layout of fn_moe_down_b on
  * the Constant BATCH_MSL page: expert u's rows start at u*NB).
- * Accumulation is f32 throughout. For a given (in_dim, nb) the result does not depend on
- * out_dim, n_mat, or which entry point (q4mv / q4mv_2row) is used: bitwise identical.
+ * Accumulation is f32 throughout. The kernel, its launch shape and its summation order are
+ * chosen from (in_dim, nb, out_dim) alone (q4mv_auto_path), never from n_mat: a matrix
+ * gives bitwise the same result alone, in a batch of n_mat, or as a slot of q4mv_experts,
+ * and q4mv and q4mv_2row give bitwise the same result. On the VALU kernels (paths 1 and 2)
+ * the result does not depend on out_dim either.
+ * Rows of any length (the page's row kernels read the activations from device memory at
+ * any row length): each workgroup stages its activation rows in LDS as f16, and where
+ * those of a whole row do not fit in the 160 KB of a gfx950 compute unit the product runs
+ * as K slices of the columns, one launch per slice in column order, each later slice adding
+ * its partial product to what y holds (y is then read as well as written). The slices
+ * depend on (in_dim, nb, out_dim) only.
  * Errors: NULL pointer; n_mat < 1, out_dim < 1, in_dim < 64, in_dim % 64 != 0,
- * nb outside 1..Q4MV_MAX_NB, nb*in_dim > Q4MV_MAX_NB_X_IN (SHAPE); w, xe or xo not 16-byte
- * aligned, scales/biases not 2-byte, xsum/y not 4-byte aligned (ALIGN); launch failure.
+ * nb outside 1..Q4MV_MAX_NB (SHAPE); w, xe or xo not 16-byte aligned, scales/biases not
+ * 2-byte, xsum/y not 4-byte aligned (ALIGN); launch failure.
  */
 int q4mv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, const void *xe,
          const void *xo, const float *xsum, float *y, int n_mat, int out_dim, int in_dim,
@@ -121,8 +127,10 @@ int q4mv(const uint32_t *w, const uint16_t *scales, const uint16_t *biases, cons
 /*
  * q4mv_2row -- same contract and bitwise-identical result; each lane group of a wavefront
  * owns two consecutive output rows and shares every activation read between them (the
- * two-row helper fn_q4_2rows_h and fn_moe_down_b on the Constant BATCH_MSL page). Pays off
- * on short rows (the 640-wide expert down projection).
+ * two-row helper fn_q4_2rows_h and fn_moe_down_b on the Constant BATCH_MSL page). It takes
+ * the MFMA kernel wherever q4mv does. (On MI355X the one-row kernel keeps its activations
+ * in registers, so there is no activation read left to share, and it measured faster than
+ * the two-row kernel on every shape, the 640-wide expert down projection included.)
  * Extra error: out_dim odd (ODD_ROWS).
  */
 int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
@@ -130,16 +138,16 @@ int q4mv_2row(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               int out_dim, int in_dim, int nb, void *stream);
 
 /*
- * q4mv_path -- q4mv with an explicit kernel choice instead of the nb-based dispatch.
+ * q4mv_path -- q4mv with an explicit kernel choice instead of the automatic dispatch.
  *   path 0: automatic (what q4mv does), 1: VALU dot-product kernel, one row per lane group,
  *   2: VALU kernel, two rows per lane group (q4mv_2row; out_dim must be even),
  *   3: MFMA kernel (16x16x32 or 32x32x16 f16 matrix cores).
- * Same arguments, layouts and errors as q4mv, plus PATH for an unknown path, and SHAPE when
- * path 3 is asked for a shape whose staged activations and sums
- * (nb*(in_dim/8+1)*16 + in_dim bytes) plus an 18 KB scratch do not fit in the 160 KB of LDS
- * (in_dim >= 48512, 29120, 20800 for nb = 1, 2, 3, and in_dim >= 16192 for nb = 4; the
- * automatic dispatch never sends those shapes there). For testing and measurement of every
- * kernel at every nb.
+ * Every path takes every nb and row length, with K slices as q4mv describes: the VALU
+ * kernels stage min(nb, 8) rows per launch (larger batches run as launches over row ranges
+ * of 8) at 2.125 bytes per value and slice where that exceeds the LDS; the MFMA kernel
+ * stages nb * (in_dim/8 + 1) * 16 + in_dim bytes next to its per-wave scratch.
+ * Same arguments, layouts and errors as q4mv, plus PATH for an unknown path. For testing and
+ * measurement of every kernel at every nb.
  */
 int q4mv_path(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
               const void *xe, const void *xo, const float *xsum, float *y, int n_mat,
@@ -226,8 +234,8 @@ int q4mv_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows
  *          two rows per lane group (out_dim even; bitwise the same result as 1), 3 the MFMA
  *          kernel (the codes moved into the Q4 nibble layout as each tile is staged, the
  *          tiled product of the page's expert GEMM fn_expert_qmm; needs in_dim/64 a
- *          multiple of 4, scales and biases 8-byte aligned, and the 8-wave launch shape of
- *          q4mv_path's path 3).
+ *          multiple of 4 and scales and biases 8-byte aligned). Long rows run as K slices
+ *          as in q4mv.
  * Errors: as q4mv (w 8-byte aligned), plus VALUE for bits, PATH for a path outside 0..3,
  * ODD_ROWS for path 2 with odd out_dim, SHAPE for path 3 where it is not accepted.
  */
@@ -293,11 +301,11 @@ int q4mv_combine(const float *y, const float *wmap, float *out, int n_u, int nb,
                  void *stream);
 
 /* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
-   (two_row = 1) takes for this shape; a negative status if the shape is invalid. nb > 3
-   runs on the MFMA kernel when its LDS footprint fits (see q4mv_path), else on the VALU
-   kernels. Below that q4mv_2row takes the two-row kernel, and q4mv the
-   one-row kernel for nb = 1 and the two-row kernel for nb = 2, 3 when out_dim is even (the
-   two VALU kernels give bitwise the same result). */
+   (two_row = 1) takes for this shape; a negative status if the shape is invalid. The MFMA
+   kernel for nb >= 4, and for nb = 2, 3 on matrices of at least 1024 32-row tiles
+   (out_dim > 32736); otherwise q4mv takes the one-row VALU kernel and q4mv_2row the two-row
+   one (the two VALU kernels give bitwise the same result). in_dim does not enter the choice:
+   every path takes every row length. */
 int q4mv_auto_path(int in_dim, int nb, int two_row, int out_dim);
 
 /* Static English text for a status code. */

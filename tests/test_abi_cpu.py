@@ -61,7 +61,7 @@ def test_gemv_validation(L, fn):
     for k in ("w", "s", "b", "xe", "xo", "xsum", "y"):
         assert f(*gemv_args(**{k: None}), None) == ENULL
     for kw in (dict(n_mat=0), dict(out=0), dict(ind=0), dict(ind=96), dict(ind=32),
-               dict(nb=0), dict(nb=17), dict(nb=16, ind=4160), dict(ind=-64)):
+               dict(nb=0), dict(nb=17), dict(ind=-64)):
         assert f(*gemv_args(**kw), None) == ESHAPE, kw
     for kw in (dict(w=A + 4), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1), dict(b=A + 1),
                dict(xsum=A + 2), dict(y=A + 1)):
@@ -100,16 +100,24 @@ def test_pack_validation(L):
 
 
 def test_auto_path(L):
-    assert L.q4mv_auto_path(2560, 1, 0, 10) == 1   # one activation row: one-row kernel
-    assert L.q4mv_auto_path(2560, 2, 0, 9) == 1    # odd out_dim: one-row kernel
-    assert L.q4mv_auto_path(2560, 2, 0, 10) == 2   # even out_dim: two-row kernel
-    assert L.q4mv_auto_path(640, 1, 1, 2560) == 2  # q4mv_2row: two-row kernel
-    assert L.q4mv_auto_path(2560, 3, 0, 2560) == 2
+    """The automatic choice depends on nb and out_dim only (never on n_mat)."""
+    assert L.q4mv_auto_path(2560, 1, 0, 10) == 1      # one activation row: one-row kernel
+    assert L.q4mv_auto_path(2560, 2, 0, 9) == 1       # short launches: one-row kernel
+    assert L.q4mv_auto_path(2560, 2, 0, 10) == 1
+    assert L.q4mv_auto_path(2560, 3, 0, 9728) == 1    # 304 tiles
+    assert L.q4mv_auto_path(640, 1, 1, 2560) == 2     # q4mv_2row: two-row kernel
+    assert L.q4mv_auto_path(2560, 3, 1, 2560) == 2
+    assert L.q4mv_auto_path(2560, 2, 0, 32768) == 3   # 1024 tiles: the MFMA kernel from 2 rows
+    assert L.q4mv_auto_path(2560, 2, 1, 32768) == 3   # q4mv_2row follows q4mv onto it
+    assert L.q4mv_auto_path(2560, 2, 0, 32737) == 3
+    assert L.q4mv_auto_path(2560, 2, 0, 32736) == 1   # 1023 tiles
     assert L.q4mv_auto_path(2560, 4, 0, 2560) == 3
     assert L.q4mv_auto_path(2560, 16, 1, 2560) == 3
+    assert L.q4mv_auto_path(8192, 16, 0, 8) == 3      # K-sliced where the row does not fit
+    assert L.q4mv_auto_path(1 << 20, 16, 0, 8) == 3
     assert L.q4mv_auto_path(640, 1, 1, 7) == EODD
     assert L.q4mv_auto_path(96, 1, 0, 8) == ESHAPE
-    assert L.q4mv_auto_path(8192, 16, 0, 8) == ESHAPE
+    assert L.q4mv_auto_path(2560, 17, 0, 8) == ESHAPE
     assert L.q4mv_auto_path(2560, 1, 0, 0) == ESHAPE
 
 
@@ -169,7 +177,7 @@ def test_experts_validation(L):
     for k in ("w", "s", "b", "sel", "xe", "xo", "xsum", "y"):
         assert f(*experts_args(**{k: None})) == ENULL, k
     for kw in (dict(n_bank=0), dict(n_sel=0), dict(n_sel=65536), dict(out=0), dict(ind=96),
-               dict(ind=32), dict(nb=0), dict(nb=17), dict(nb=16, ind=4160)):
+               dict(ind=32), dict(nb=0), dict(nb=17)):
         assert f(*experts_args(**kw)) == ESHAPE, kw
     for kw in (dict(w=A + 4), dict(sel=A + 2), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1),
                dict(b=A + 1), dict(xsum=A + 2), dict(y=A + 1)):
@@ -177,8 +185,6 @@ def test_experts_validation(L):
     assert f(*experts_args(path=4)) == EPATH
     assert f(*experts_args(path=-1)) == EPATH
     assert f(*experts_args(path=2, out=7)) == EODD
-    # the MFMA path's LDS limit, as q4mv_path
-    assert f(*experts_args(path=3, nb=4, ind=16192)) == ESHAPE
 
 
 def test_combine_validation(L):
@@ -199,7 +205,7 @@ def test_lowbit_validation(L):
         for k in ("w", "s", "b", "xe", "xo", "xsum", "y"):
             assert f(bits, *gemv_args(**{k: None}), 0, None) == ENULL, k
         for kw in (dict(n_mat=0), dict(out=0), dict(ind=96), dict(ind=32), dict(nb=0),
-                   dict(nb=17), dict(nb=16, ind=4160)):
+                   dict(nb=17)):
             assert f(bits, *gemv_args(**kw), 0, None) == ESHAPE, kw
         for kw in (dict(w=A + 4), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1), dict(xsum=A + 2),
                    dict(y=A + 1)):
@@ -233,8 +239,7 @@ def test_fused_validation(L):
                 a["nb"], a["path"], None]
     for k in ("w", "s", "b", "x", "y"):
         assert L.q4mv_fused(*args(**{k: None})) == ENULL
-    for kw in (dict(n_mat=0), dict(out=0), dict(ind=96), dict(nb=0), dict(nb=17),
-               dict(nb=16, ind=4160)):
+    for kw in (dict(n_mat=0), dict(out=0), dict(ind=96), dict(nb=0), dict(nb=17)):
         assert L.q4mv_fused(*args(**kw)) == ESHAPE, kw
     for kw in (dict(w=A + 4), dict(x=A + 8), dict(s=A + 1), dict(y=A + 2)):
         assert L.q4mv_fused(*args(**kw)) == EALIGN, kw

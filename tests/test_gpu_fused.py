@@ -18,9 +18,6 @@ def check_paths(d, what, out_dim):
     for path in PATHS:
         if path == q4.PATH_VALU_2ROW and out_dim % 2:
             continue
-        if path == q4.PATH_MFMA and d["nb"] > 3 and \
-                q4.q4mv_auto_path(d["w"].shape[2] * 8, d["nb"], False, out_dim) != q4.PATH_MFMA:
-            continue  # the MFMA kernel's LDS does not fit this shape
         flush(f"[fused] {what} path={path}")
         want = q4.q4mv_path(d["w"], d["s"], d["b"], d["xe"], d["xo"], d["xsum"], d["nb"], path)
         got = q4.q4mv_fused(d["w"], d["s"], d["b"], d["x"], d["nb"], path)

@@ -26,9 +26,9 @@ def upload_lowbit(case, bits):
 
 
 def mfma_ok(in_dim, nb, out_dim):
-    """Whether q4mv_lowbit accepts path 3 for the shape (8-wave MFMA blocks, groups % 4)."""
-    return (in_dim // 64) % 4 == 0 and (nb > 3 or in_dim < 20800) and \
-        q4.q4mv_auto_path(in_dim, max(nb, 4), False, out_dim) == q4.PATH_MFMA
+    """Whether q4mv_lowbit accepts path 3 for the shape (groups per row a multiple of 4; long
+    rows run as K slices)."""
+    return (in_dim // 64) % 4 == 0
 
 
 def run(d, bits, path):
