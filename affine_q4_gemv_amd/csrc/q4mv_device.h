@@ -19,6 +19,16 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 // subnormal q * 2^-24 (exact); the kernels accumulate in those units and rescale once.
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kTwoM24 = 5.9604644775390625e-08f;
+constexpr float kTwo20 = 1048576.0f;
+constexpr float kTwoM20 = 9.5367431640625e-07f;
+
+// Whether either f16 of a pair has magnitude 4096 or more (or is NaN): 16 times it would
+// not be finite in f16.
+__device__ __forceinline__ int f16x2_big(half2_t p)
+{
+    const uint32_t v = __builtin_bit_cast(uint32_t, p);
+    return (int)((v & 0x7FFFu) >= 0x6C00u) | (int)(((v >> 16) & 0x7FFFu) >= 0x6C00u);
+}
 
 // bf16 bit pattern (in the low 16 bits) -> f32: the bits are the high half of the f32.
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }

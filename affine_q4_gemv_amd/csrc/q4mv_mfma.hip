@@ -10,9 +10,9 @@
 // slice lies inside one group, and the four MFMAs of a group sum to that group's sum(q*x)
 // for every (activation row, output row). A word's eight codes become one B operand: the
 // masks give (c0,c4), 16*(c1,c5), (c2,c6), 16*(c3,c7), and the matching activations are
-// staged as (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16, so a single accumulator holds
-// sum(q*x) (the /16 is exact in f16 for |x| >= 2^-10; below that it is the f16 rounding of a
-// subnormal, at most 2^-25 in x/16). The group's scale and bias are then applied in f32 (the
+// staged as 16*(x0,x4), (x1,x5), 16*(x2,x6), (x3,x7) (exact in f16 while the staged |x| stay
+// below 4096; else (x0,x4), (x1,x5)/16, ..., see the staging), so a single accumulator holds
+// 16*sum(q*x). The group's scale and bias are then applied in f32 (the
 // per-group fold of fn_q4_rows_h, Constant BATCH_MSL page, quantized_rows section). The
 // dequantised weight is never formed (the page's tiled expert GEMM dequantises to f16 tiles
 // instead). With 16x16x32 the tile is two 16-row halves: lane (n16, kb) (kb = lane / 16)
@@ -160,7 +160,9 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // the lanes that hold activation rows below nb).
     const int RS = 4 * C + 1;
     float4_t *const xsg_w = reinterpret_cast<float4_t *>(lds + nb * RS);
-    float *const part = reinterpret_cast<float *>(xsg_w + groups * 4);
+    // one int per wave for the staging scale vote (32 bytes), then the partial sums
+    int *const vote = reinterpret_cast<int *>(xsg_w + groups * 4);
+    float *const part = reinterpret_cast<float *>(vote + 8);
     // lanes whose accumulators hold activation rows below nb (16x16x32: rows 4kb .. 4kb+3)
     const int plan = MF16 ? 16 * ((nb + 3) >> 2) : 64;
     uint4 *const scratch_all =
@@ -168,21 +170,32 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 
     // Stage activations and group sums. Called after each wave has issued its first weight
     // loads, so the two latencies overlap.
-    // Fused prep (xf non-null: f32 activations): the f16 rounding, the 1/16 of the odd
-    // pair members and the chunk sums of q4mv_prepare_x done here with the same additions
-    // (pair sums, a balanced tree over a chunk's 16 pairs: each thread adds its word's four
-    // pairs, two quad DPP steps add the chunk's four words; then a group's two chunks in
-    // order), so the LDS contents are bitwise those staged from q4mv_prepare_x's outputs.
-    // One thread per 8-column word; a quad of lanes is one chunk, 8 lanes one group (words
-    // per row are a multiple of 8). With xf_glu the rows are [gate | up] and the values
-    // silu(gate) * up (as q4mv_swiglu_prep forms them).
-    auto fstage = [&]() {
+    // Staging scale. A word's codes split into the pairs (c0,c4), 16 (c1,c5), (c2,c6),
+    // 16 (c3,c7) (masked nibbles as f16 subnormals). The matching activation pairs are staged
+    // as 16 x (even pairs) and x (odd pairs), both exact in f16 while every staged |x| is
+    // below 4096, so each product is 16 c x, the group sums are staged times 16 as well, and
+    // the store scales by 2^20 (up = true). If a staged |x| reaches 4096 (16 x would
+    // overflow), the block stages again with x (even) and x/16 (odd; exact for |x| >= 2^-10,
+    // else rounded to the f16 subnormal spacing) and the store scales by 2^24. The choice
+    // depends only on the staged rows, so every block of a matrix makes the same one.
+    // Fused prep (xf non-null: f32 activations): the f16 rounding and the chunk sums of
+    // q4mv_prepare_x done here with the same additions (pair sums, a balanced tree over a
+    // chunk's 16 pairs: each thread adds its word's four pairs, two quad DPP steps add the
+    // chunk's four words; then a group's two chunks in order), so the LDS contents are
+    // bitwise those staged from q4mv_prepare_x's outputs. One thread per 8-column word; a
+    // quad of lanes is one chunk, 8 lanes one group (words per row are a multiple of 8). With
+    // xf_glu the rows are [gate | up] and the values silu(gate) * up (as q4mv_swiglu_prep
+    // forms them). Returns whether this thread saw an |x| of 4096 or more.
+    auto fstage = [&](bool up) {
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
         const int rs4 = xf_glu ? in_full >> 1 : in_full >> 2;  // float4 per row
         const float4 *xf_m = reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4;
         const int wrow = in_dim >> 3, words = nb * wrow;
         float *xsw = reinterpret_cast<float *>(xsg_w);
-        const _Float16 sixteenth = (_Float16)0.0625f;
+        const half2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
+        const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const float sum_scale = up ? kTwoM20 : kTwoM24;
+        int big = 0;
         for (int base = threadIdx.x; base < words; base += 2 * TH) {
             float4 v[2][4];
 #pragma unroll
@@ -209,32 +222,35 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                     sum += dpp<0xB1>(sum);
                     sum += dpp<0x4E>(sum);
                     const float other = __shfl_xor(sum, 4, 64);  // the group's other chunk
-                    if ((kw & 7) == 0) xsw[(kw >> 3) * 16 + r] = (sum + other) * kTwoM24;
-                    // unit r*RS + 4c + j: (x0, x4) (x1/16, x5/16) (x2, x6) (x3/16, x7/16)
+                    if ((kw & 7) == 0) xsw[(kw >> 3) * 16 + r] = (sum + other) * sum_scale;
+                    // unit r*RS + 4c + j: the pairs (x0, x4) (x1, x5) (x2, x6) (x3, x7)
+                    const half2_t p0 = {h[0], h[4]}, p1 = {h[1], h[5]}, p2 = {h[2], h[6]},
+                                  p3 = {h[3], h[7]};
+                    big |= f16x2_big(p0) | f16x2_big(p1) | f16x2_big(p2) | f16x2_big(p3);
                     uint4 u;
-                    u.x = __builtin_bit_cast(uint32_t, half2_t{h[0], h[4]});
-                    u.y = __builtin_bit_cast(uint32_t, half2_t{h[1] * sixteenth, h[5] * sixteenth});
-                    u.z = __builtin_bit_cast(uint32_t, half2_t{h[2], h[6]});
-                    u.w = __builtin_bit_cast(uint32_t, half2_t{h[3] * sixteenth, h[7] * sixteenth});
+                    u.x = __builtin_bit_cast(uint32_t, up ? p0 * sixteen : p0);
+                    u.y = __builtin_bit_cast(uint32_t, up ? p1 : p1 * sixteenth);
+                    u.z = __builtin_bit_cast(uint32_t, up ? p2 * sixteen : p2);
+                    u.w = __builtin_bit_cast(uint32_t, up ? p3 : p3 * sixteenth);
                     lds[r * RS + kw] = u;
                 }
             }
         }
         for (int u = threadIdx.x; u < groups * 16; u += TH)
             if ((u & 15) >= nb) xsw[u] = 0.0f;
-        __syncthreads();
+        return big;
     };
-    auto stage = [&]() {
-        if (xf) {
-            fstage();
-            return;
-        }
+    // the same from q4mv_prepare_x's outputs (xf null)
+    auto pstage = [&](bool up) {
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
         const uint2 *xe_m = xe + xrow0 * words8 + (k0 >> 3);
         const uint2 *xo_m = xo + xrow0 * words8 + (k0 >> 3);
         const float *xsum_m = xsum + xrow0 * Cf + kc0;
         const int units = nb * C * 4;  // one per (row, chunk, word)
+        const half2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
         const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const float sum_scale = up ? kTwoM20 : kTwoM24;
+        int big = 0;
         // each round issues all of its loads before any LDS write: one memory round trip
         for (int base = threadIdx.x; base < units; base += 4 * TH) {
             uint2 e[4], o[4];
@@ -252,10 +268,15 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                 if (u < units) {
                     const int r = u / (C * 4), cw = u - r * (C * 4);
                     uint4 pr = make_pairs(e[i], o[i]);
-                    pr.y = __builtin_bit_cast(uint32_t,
-                                              __builtin_bit_cast(half2_t, pr.y) * sixteenth);
-                    pr.w = __builtin_bit_cast(uint32_t,
-                                              __builtin_bit_cast(half2_t, pr.w) * sixteenth);
+                    const half2_t p0 = __builtin_bit_cast(half2_t, pr.x);
+                    const half2_t p1 = __builtin_bit_cast(half2_t, pr.y);
+                    const half2_t p2 = __builtin_bit_cast(half2_t, pr.z);
+                    const half2_t p3 = __builtin_bit_cast(half2_t, pr.w);
+                    big |= f16x2_big(p0) | f16x2_big(p1) | f16x2_big(p2) | f16x2_big(p3);
+                    pr.x = __builtin_bit_cast(uint32_t, up ? p0 * sixteen : p0);
+                    pr.y = __builtin_bit_cast(uint32_t, up ? p1 : p1 * sixteenth);
+                    pr.z = __builtin_bit_cast(uint32_t, up ? p2 * sixteen : p2);
+                    pr.w = __builtin_bit_cast(uint32_t, up ? p3 : p3 * sixteenth);
                     lds[r * RS + cw] = pr;
                 }
             }
@@ -265,9 +286,27 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
             const int g = u >> 4, r = u & 15;
             const int rr = min(r, nb - 1);
             const float a = xsum_m[(size_t)rr * Cf + 2 * g], b = xsum_m[(size_t)rr * Cf + 2 * g + 1];
-            xsw[u] = r < nb ? (a + b) * kTwoM24 : 0.0f;
+            xsw[u] = r < nb ? (a + b) * sum_scale : 0.0f;
         }
+        return big;
+    };
+    // stages with the x16 scale unless a staged |x| reaches 4096; returns the output scale.
+    // Each wave writes its own vote (so nothing needs clearing first); after the barrier
+    // every thread reads all of them.
+    auto stage = [&]() {
+        const int mine = __any(xf ? fstage(true) : pstage(true)) ? 1 : 0;
+        if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = mine;
         __syncthreads();
+        int big = 0;
+#pragma unroll
+        for (int i = 0; i < WPB; i++) big |= vote[i];
+        if (!big) return kTwo20;
+        if (xf)
+            fstage(false);
+        else
+            pstage(false);
+        __syncthreads();
+        return kTwo24;
     };
     const float4_t *xsg = xsg_w;
 
@@ -433,7 +472,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     advance(abase, aui);
     if (more(abase)) load(abase + slot, unit_quad(aui), aui, c1, s1);
     advance(abase, aui);
-    stage();  // every wave joins the staging barrier exactly once
+    const float yscale = stage();  // every wave joins the staging barriers
     if (!more(base)) return;
     auto step_unit = [&](u32x4 (&cc)[4], SbRegs &sb) {
         const int tile = base + slot;
@@ -565,7 +604,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                     const int r = MF16 ? 4 * kb + (i % 4) : 8 * (i / 4) + 4 * h + (i % 4);
                     // the shifted last tile stores only rows that no earlier tile stores
                     if (tile < tiles && orow >= tile * 32 && orow < out_dim && r < nb) {
-                        float v = acc[i] * kTwo24;
+                        float v = acc[i] * yscale;
                         // K slices after the first add to what the earlier slices stored;
                         // only the last slice has a nonzero epi_div
                         if (accum) v += y_m[(size_t)r * out_dim + orow];

@@ -18,3 +18,15 @@ def oracle_lib():
     import oracle
     oracle.build(force=not os.path.exists(os.path.join(ROOT, "oracle", "libq4ref.so")))
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _small_results_rel_l2():
+    """Applies the relative L2 bar to the pooled small results of a GPU parity test."""
+    mod = sys.modules.get("q4_gpu")
+    if mod is not None:
+        mod.SMALL.clear()
+    yield
+    mod = sys.modules.get("q4_gpu")
+    if mod is not None:
+        mod.check_small_pool()

@@ -9,7 +9,7 @@ import torch
 
 import affine_q4_gemv_amd as q4
 import workloads
-from q4_gpu import ELEM, REL_L2, bf16_tensor, dev, flush, parity, upload
+from q4_gpu import ELEM, REL_L2, bf16_tensor, dev, flush, parity, seeds_for, upload
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -39,18 +39,20 @@ def run(d, path, y=None):
 @pytest.mark.parametrize("shape", SHAPES, ids=["x".join(map(str, s)) for s in SHAPES])
 def test_kslice_parity(oracle_lib, shape):
     n_mat, out_dim, in_dim, nb = shape
-    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=sum(shape) + 11)
-    y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
-    d = upload(case)
-    ys = {}
-    for path in PATHS:
-        if out_dim % 2 and path in ("2row", q4.PATH_VALU_2ROW):
-            continue
-        flush(f"[kslice] {shape} path={path}")
-        # y starts as garbage: the first slice must overwrite it, not add to it
-        y0 = torch.full((n_mat, nb, out_dim), 1e30, dtype=torch.float32, device=dev())
-        ys[path] = run(d, path, y=y0)
-        parity(ys[path].cpu().numpy(), y_ref, bound, f"{shape} path={path}")
+    for k in range(seeds_for(n_mat * nb * out_dim)):
+        case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=sum(shape) + 11 + 1000 * k)
+        y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
+        d = upload(case)
+        ys = {}
+        for path in PATHS:
+            if out_dim % 2 and path in ("2row", q4.PATH_VALU_2ROW):
+                continue
+            flush(f"[kslice] {shape} seed {k} path={path}")
+            # y starts as garbage: the first slice must overwrite it, not add to it
+            y0 = torch.full((n_mat, nb, out_dim), 1e30, dtype=torch.float32, device=dev())
+            ys[path] = run(d, path, y=y0)
+            parity(ys[path].cpu().numpy(), y_ref, bound, f"{shape} seed {k} path={path}",
+                   key=f"{shape} path={path}")
     # the two VALU kernels slice alike and stay bitwise equal; q4mv_2row follows q4mv
     if out_dim % 2 == 0:
         assert torch.equal(ys[q4.PATH_VALU], ys[q4.PATH_VALU_2ROW])

@@ -9,7 +9,7 @@ import torch
 
 import affine_q4_gemv_amd as q4
 import workloads
-from q4_gpu import bf16_tensor, dev, flush, parity
+from q4_gpu import bf16_tensor, dev, flush, parity, seeds_for
 
 pytestmark = pytest.mark.gpu
 
@@ -86,16 +86,19 @@ RAGGED = [(1, 1, 64, 1), (1, 77, 192, 3), (2, 33, 4160, 2), (1, 130, 640, 16),
 @pytest.mark.parametrize("n_mat,out_dim,in_dim,nb", RAGGED,
                          ids=[f"{m}x{o}x{i}-nb{b}" for m, o, i, b in RAGGED])
 def test_lowbit_ragged(oracle_lib, bits, n_mat, out_dim, in_dim, nb):
-    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=90 + out_dim)
-    y_ref, bound = oracle_lib.gemv_lowbit(bits, case["codes"], case["scales"], case["biases"],
-                                          case["x"])
-    d = upload_lowbit(case, bits)
     paths = [1, 2] if out_dim % 2 == 0 else [1]
     if mfma_ok(in_dim, nb, out_dim):
         paths.append(3)
-    for path in paths:
-        flush(f"[lowbit ragged] bits={bits} {n_mat}x{out_dim}x{in_dim} nb={nb} path={path}")
-        parity(run(d, bits, path).cpu().numpy(), y_ref, bound, f"Q{bits} path {path}")
+    for k in range(seeds_for(n_mat * nb * out_dim)):
+        case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=90 + out_dim + 1000 * k)
+        y_ref, bound = oracle_lib.gemv_lowbit(bits, case["codes"], case["scales"],
+                                              case["biases"], case["x"])
+        d = upload_lowbit(case, bits)
+        for path in paths:
+            flush(f"[lowbit ragged] bits={bits} {n_mat}x{out_dim}x{in_dim} nb={nb} seed {k} "
+                  f"path={path}")
+            parity(run(d, bits, path).cpu().numpy(), y_ref, bound, f"Q{bits} seed {k} path {path}",
+                   key=f"Q{bits} path {path}")
 
 
 @pytest.mark.parametrize("bits", [2, 3])

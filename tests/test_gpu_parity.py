@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads
-from q4_gpu import flush, parity, run, upload
+from q4_gpu import flush, parity, run, seeds_for, upload
 import affine_q4_gemv_amd as q4
 
 pytestmark = [pytest.mark.gpu,
@@ -68,7 +68,7 @@ def test_config_parity(oracle_lib, name, nb):
         parity(y, y_ref, bound, f"{name} nb={nb} path={path}")
 
 
-@pytest.mark.parametrize("nb", [1, 16])
+@pytest.mark.parametrize("nb", [1, 4, 8, 16])
 def test_lm_head_sampled(oracle_lib, nb):
     """The LM head at full size in the launch configuration the benchmark times."""
     case = workloads.make_case("lm_head", nb=nb)
@@ -96,12 +96,14 @@ RAGGED = [(1, 1, 64, 1), (2, 3, 128, 2), (3, 5, 192, 3), (1, 257, 320, 1), (2, 1
 @pytest.mark.parametrize("shape", RAGGED, ids=["x".join(map(str, s)) for s in RAGGED])
 def test_ragged_shapes(oracle_lib, shape):
     n_mat, out_dim, in_dim, nb = shape
-    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=sum(shape))
-    y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
-    d = upload(case)
-    for path in paths_for(out_dim):
-        flush(f"[ragged] {shape} path={path}")
-        parity(run(d, path).cpu().numpy(), y_ref, bound, f"{shape} path={path}")
+    for k in range(seeds_for(n_mat * nb * out_dim)):
+        case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=sum(shape) + 1000 * k)
+        y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
+        d = upload(case)
+        for path in paths_for(out_dim):
+            flush(f"[ragged] {shape} seed {k} path={path}")
+            parity(run(d, path).cpu().numpy(), y_ref, bound, f"{shape} seed {k} path={path}",
+                   key=f"{shape} path={path}")
 
 
 # many tiles (the MFMA kernel's 16x16x32 range: at least 1024 tiles, K-split <= 2, nb
@@ -148,3 +150,40 @@ def test_block_loaded_scales(oracle_lib, shape):
         assert d[name].data_ptr() % 16 == 8
     flush(f"[block scales] {shape} 8-byte aligned scales")
     assert torch.equal(run(d, q4.PATH_VALU), y1)
+
+
+# Small activations: the MFMA kernel stages activations as 16 x and x (exact in f16), so its
+# error stays that of the f16 activation format itself, like the VALU kernels'. Few and many
+# tiles (32x32x16 and 16x16x32 matrix-core shapes).
+SMALL_X = [(1, 2560, 2560, 4), (1, 512, 2560, 16), (1, 40000, 512, 4)]
+
+
+@pytest.mark.parametrize("x_scale", [1e-3, 1e-4])
+@pytest.mark.parametrize("shape", SMALL_X, ids=["x".join(map(str, s)) for s in SMALL_X])
+def test_small_activations(oracle_lib, shape, x_scale):
+    n_mat, out_dim, in_dim, nb = shape
+    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=sum(shape) + 3, x_scale=x_scale)
+    y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
+    d = upload(case)
+    for path in (q4.PATH_AUTO, q4.PATH_VALU, q4.PATH_MFMA):
+        flush(f"[small x] {shape} x_scale={x_scale} path={path}")
+        parity(run(d, path).cpu().numpy(), y_ref, bound, f"{shape} x{x_scale} path={path}")
+
+
+# Activations of 4096 or more: 16 x would overflow f16, so the MFMA kernel stages those rows'
+# block with x and x/16 instead (output scale 2^24); rows just below stay on the x16 staging.
+@pytest.mark.parametrize("peak", [4094.0, 4096.0, 6.0e4])
+def test_large_activations(oracle_lib, peak):
+    n_mat, out_dim, in_dim, nb = 2, 300, 1024, 4
+    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=int(peak) % 97)
+    case["x"][1, 2, 77] = peak          # an even column of matrix 1
+    case["x"][0, 0, 513] = -peak / 2    # an odd column of matrix 0
+    y_ref, bound = oracle_lib.gemv(case["codes"], case["scales"], case["biases"], case["x"])
+    d = upload(case)
+    for path in (q4.PATH_VALU, q4.PATH_MFMA):
+        flush(f"[large x] peak={peak} path={path}")
+        y = run(d, path)
+        parity(y.cpu().numpy(), y_ref, bound, f"peak {peak} path={path}")
+        fused = q4.q4mv_fused(d["w"], d["s"], d["b"], d["x"], nb, path)
+        torch.cuda.synchronize()
+        assert torch.equal(fused, y), f"peak {peak} path={path}: fused differs"

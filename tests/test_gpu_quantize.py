@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import affine_q4_gemv_amd as q4
+import quant_ties
 import workloads
 from q4_gpu import ELEM, dev, flush
 
@@ -30,10 +31,13 @@ def weights(n, k, seed):
         wf[1, :64] = -0.25 + (np.arange(64) % 16) * 2.0 ** -6  # exact grid
         wf[2, :64] = rng.normal(0, 1e4, 64)                  # large magnitudes
         wf[3, :64] = rng.normal(0, 1e-30, 64)                # tiny: 1/d overflows -> id = 0
+    if n >= 8 and k >= 128:
+        # codes, scales and biases on exact rounding ties (round half to even)
+        wf[4:8, :128] = quant_ties.tie_rows()[0]
     return wf
 
 
-@pytest.mark.parametrize("n,k", [(4, 128), (37, 640), (300, 2560), (9728, 2560)])
+@pytest.mark.parametrize("n,k", [(8, 128), (37, 640), (300, 2560), (9728, 2560)])
 def test_quantize_bit_exact(oracle_lib, n, k):
     wf = weights(n, k, seed=n + k)
     flush(f"[quantize] {n}x{k}")
@@ -43,6 +47,15 @@ def test_quantize_bit_exact(oracle_lib, n, k):
     np.testing.assert_array_equal(unpack(w), q_ref)
     np.testing.assert_array_equal(bits(s), s_ref)
     np.testing.assert_array_equal(bits(b), b_ref)
+    # the tie groups against the values the rounding rule itself gives
+    _, codes, s_want, b_want = quant_ties.tie_rows()
+    got_q, got_s, got_b = unpack(w), bits(s), bits(b)
+    for (r, g), c in codes.items():
+        np.testing.assert_array_equal(got_q[4 + r, 64 * g:64 * g + 64], c)
+    for (r, g), want in s_want.items():
+        assert int(got_s[4 + r, g]) == want
+    for (r, g), want in b_want.items():
+        assert int(got_b[4 + r, g]) == want
 
 
 def test_quantize_then_gemv(oracle_lib):

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import quant_ties
 import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -379,38 +380,98 @@ def test_swiglu_closed_forms(oracle_lib):
 
 
 # --- affine-Q4 quantiser (steps of host_quant_q5_row, memra-engine qwen4exp_gpu.rs page) ----
+# The pins take the quantiser under test, so planted mistakes can be run through them.
 
-def test_quantize_reconstruction_bound(oracle_lib):
+def qpin_reconstruction_bound(quantize):
     # every weight is within d/2 of d*q + mn (the rounding step), up to f32 slack, and the
     # group's minimum gets code 0 and its maximum code 15
     rng = np.random.default_rng(3)
     wf = (rng.normal(0, 0.02, (6, 512)) + rng.normal(0, 0.1, (6, 1))).astype(np.float32)
-    q, s_bits, b_bits, d, mn = oracle_lib.quantize(wf)
+    q, s_bits, b_bits, d, mn = quantize(wf)
     g = wf.reshape(6, 8, 64).astype(np.float64)
     rec = d[:, :, None].astype(np.float64) * q.reshape(6, 8, 64) + mn[:, :, None]
     slack = 4 * 2.0 ** -24 * (np.abs(g).max(axis=2) + 15 * d)[:, :, None]
-    assert np.all(np.abs(rec - g) <= d[:, :, None] / 2 + slack)
+    ok = np.all(np.abs(rec - g) <= d[:, :, None] / 2 + slack)
     qq = q.reshape(6, 8, 64)
-    assert np.all(qq[np.arange(6)[:, None], np.arange(8)[None, :], g.argmin(axis=2)] == 0)
-    assert np.all(qq[np.arange(6)[:, None], np.arange(8)[None, :], g.argmax(axis=2)] == 15)
+    ok &= np.all(qq[np.arange(6)[:, None], np.arange(8)[None, :], g.argmin(axis=2)] == 0)
+    ok &= np.all(qq[np.arange(6)[:, None], np.arange(8)[None, :], g.argmax(axis=2)] == 15)
     # the stored bf16 values decode to within half a bf16 ulp (2^-8 relative) of d and mn
-    sd = workloads.bf16_bits_to_f32(s_bits).astype(np.float64)
-    bd = workloads.bf16_bits_to_f32(b_bits).astype(np.float64)
-    assert np.all(np.abs(sd - d) <= 2.0 ** -8 * np.abs(d))
-    assert np.all(np.abs(bd - mn) <= 2.0 ** -8 * np.abs(mn))
+    sd = bf16_torch(s_bits)
+    bd = bf16_torch(b_bits)
+    ok &= np.all(np.abs(sd - d) <= 2.0 ** -8 * np.abs(d))
+    ok &= np.all(np.abs(bd - mn) <= 2.0 ** -8 * np.abs(mn))
+    return bool(ok)
 
 
-def test_quantize_closed_forms(oracle_lib):
-    # a group on an exact grid mn + k*2^-6 (k = 0..15) gets codes k; a constant group gets
-    # d = 0, codes 0 and bias = the constant
+def qpin_closed_forms(quantize):
+    # a group on an exact grid mn + k*2^-6 (k = 0..15) gets codes k, d = 2^-6 and bias mn; a
+    # constant group gets d = 0, codes 0 and bias = the constant
     k = np.arange(64) % 16
     wf = np.stack([-0.25 + k * 2.0 ** -6, np.full(64, 0.75)]).astype(np.float32)
-    q, s_bits, b_bits, d, mn = oracle_lib.quantize(wf)
-    np.testing.assert_array_equal(q[0], k)
-    assert d[0, 0] == np.float32(2.0 ** -6) and mn[0, 0] == np.float32(-0.25)
-    np.testing.assert_array_equal(q[1], 0)
-    assert d[1, 0] == 0 and s_bits[1, 0] == 0
-    assert workloads.bf16_bits_to_f32(b_bits[1:2, :1])[0, 0] == np.float32(0.75)
+    q, s_bits, b_bits, d, mn = quantize(wf)
+    return bool(np.array_equal(q[0], k) and d[0, 0] == np.float32(2.0 ** -6)
+                and mn[0, 0] == np.float32(-0.25) and s_bits[0, 0] == 0x3C80
+                and b_bits[0, 0] == 0xBE80 and np.all(q[1] == 0) and d[1, 0] == 0
+                and s_bits[1, 0] == 0 and b_bits[1, 0] == 0x3F40)
+
+
+def qpin_code_ties(quantize):
+    # (w - mn) / d lands exactly on k + 1/2: round half to even (round_ties_even)
+    rows, codes, _, _ = quant_ties.tie_rows()
+    q = quantize(rows)[0]
+    return all(np.array_equal(q[r, 64 * g:64 * g + 64], c) for (r, g), c in codes.items())
+
+
+def qpin_bf16_ties(quantize):
+    # d and mn whose f32 low half is exactly 0x8000: stored rounded to nearest even
+    rows, _, s_want, b_want = quant_ties.tie_rows()
+    _, s_bits, b_bits, _, _ = quantize(rows)
+    return (all(int(s_bits[r, g]) == w for (r, g), w in s_want.items())
+            and all(int(b_bits[r, g]) == w for (r, g), w in b_want.items()))
+
+
+QPINS = [qpin_reconstruction_bound, qpin_closed_forms, qpin_code_ties, qpin_bf16_ties]
+
+
+@pytest.mark.parametrize("pin", QPINS, ids=[p.__name__ for p in QPINS])
+def test_quantize_pin(oracle_lib, pin):
+    assert pin(oracle_lib.quantize)
+
+
+# planted mistakes in the quantiser (text edits of the oracle's own source, run on the CPU):
+# each must fail at least one pin
+QMUTANTS = {
+    "code_round_half_up": ("t = np.rint((g - mn[:, :, None]) * inv[:, :, None])",
+                           "t = np.floor((g - mn[:, :, None]) * inv[:, :, None] + np.float32(0.5))"),
+    "code_truncate": ("t = np.rint((g - mn[:, :, None]) * inv[:, :, None])",
+                      "t = np.trunc((g - mn[:, :, None]) * inv[:, :, None])"),
+    "bf16_round_half_up": ("return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)",
+                           "return ((u + 0x8000) >> 16).astype(np.uint16)"),
+    "bf16_truncate": ("return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)",
+                      "return (u >> 16).astype(np.uint16)"),
+    "sixteen_steps": ("d = ((mx - mn) / np.float32(15.0)).astype(np.float32)",
+                      "d = ((mx - mn) / np.float32(16.0)).astype(np.float32)"),
+    "bias_is_max": ("return q, _bf16_rne_bits(d), _bf16_rne_bits(mn), d, mn",
+                    "return q, _bf16_rne_bits(d), _bf16_rne_bits(mx), d, mn"),
+    "codes_clipped_at_14": ("q = np.clip(t, 0, 15)", "q = np.clip(t, 0, 14)"),
+}
+
+
+def test_quantize_mutants_are_caught():
+    path = os.path.join(ROOT, "oracle", "__init__.py")
+    src = open(path).read()
+    for name, (old, new) in QMUTANTS.items():
+        assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+        ns = {"__name__": f"oracle_mutant_{name}", "__file__": path}
+        exec(compile(src.replace(old, new), f"<{name}>", "exec"), ns)
+        failed = []
+        for pin in QPINS:
+            try:
+                if not pin(ns["quantize"]):
+                    failed.append(pin.__name__)
+            except Exception:
+                failed.append(pin.__name__)
+        assert failed, f"mutant {name} passed every quantiser pin"
 
 
 def test_quantize_then_gemv(oracle_lib):
@@ -582,3 +643,21 @@ def test_lowbit_decomposition(oracle_lib):
     ys, bs = oracle_lib.gemv_lowbit(3, case["codes"], case["scales"], case["biases"], case["x"],
                                     rows=[23, 0, 5])
     assert np.array_equal(ys, y[:, :, [23, 0, 5]]) and np.array_equal(bs, bound[:, :, [23, 0, 5]])
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_oracle_under_sanitizers(tmp_path):
+    """The C oracle built with AddressSanitizer and UndefinedBehaviorSanitizer (host code
+    only) runs exactly-sized buffers through both entry points with no report."""
+    exe = tmp_path / "q4ref_sanitized"
+    subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-pthread",
+                    os.path.join(ROOT, "oracle", "q4ref.c"),
+                    os.path.join(ROOT, "tests", "sanitize_oracle.c"), "-o", str(exe), "-lm"],
+                   check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
+    assert "all checks passed" in r.stdout
