@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 600e6  # > 2 x (256 MB Infinity Cache + L2)
 CALIB_BYTES = 256 << 20
+MAX_COPIES = 200  # launches per timed graph
 METRIC = "affine-Q4 GEMV weight GB/s and % of HBM peak at NB=1/4/8; rows/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4mv_traffic.json")
 
@@ -98,7 +99,9 @@ class Problem:
             return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
         s0, b0 = bf16(c["scales"]), bf16(c["biases"])
-        self.R = max(1, math.ceil(ROTATE_BYTES / self.weight_bytes)) if rotate else 1
+        # copies past MAX_COPIES are never read by a graph of that many launches
+        self.R = min(MAX_COPIES, max(1, math.ceil(ROTATE_BYTES / self.weight_bytes))) \
+            if rotate else 1
         self.w = [w0] + [w0.clone() for _ in range(self.R - 1)]
         self.s = [s0] + [s0.clone() for _ in range(self.R - 1)]
         self.b = [b0] + [b0.clone() for _ in range(self.R - 1)]
@@ -142,38 +145,24 @@ class Problem:
                          y=self.y)
 
     def _graph(self, body, n):
-        """Capture n iterations of body(i) in a HIP graph (after one eager warm-up)."""
-        torch = self.torch
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for i in range(2):
-                body(i)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                body(i)
-        return g
+        """Capture n iterations of body(i) in a HIP graph (after two eager warm-ups)."""
+        return _capture(self.torch, body, n)
 
-    def _time_graph(self, g, n, warmup_replays=1, reps=3):
-        """Median ms per iteration over reps replays of g (n iterations each); the per-replay
-        figures are kept in self.trials."""
-        torch = self.torch
-        for _ in range(warmup_replays):
-            g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b) / n)
-        self.trials = ts
-        return statistics.median(ts)
+    def time_path(self, path, launches=200):
+        """Average ms of a fused launch (prep inside) on a forced kernel path."""
+        q4 = self.q4
+
+        def body(i):
+            k = i % self.R
+            q4.q4mv_fused(self.w[k], self.s[k], self.b[k], self.x, self.nb, path=path, y=self.y)
+        return self._time_graph(self._graph(body, launches), launches, reps=5)
+
+    def _time_graph(self, g, n, warmup_replays=1, reps=3, warm=None):
+        """Median ms per iteration over reps timed replays of g (n iterations each); the
+        per-replay figures are kept in self.trials. Each timed replay follows an untimed
+        replay of `warm` (default g) with nothing in between, so the GPU is busy when the
+        first timed launch starts; the events bracket exactly the n timed iterations."""
+        return time_graph(self.torch, g, n, warmup_replays, reps, warm, self)
 
     def check_graph_output(self):
         """The graph's result equals an eager call bit for bit (weights copies are equal);
@@ -370,6 +359,126 @@ class MoeLayer(MoeChain):
         q4.q4mv_combine(self.yd, self.wmap, out=self.y)
 
 
+WARM_S = 0.3  # untimed warm-up before the first timed trial, seconds of GPU work
+
+
+def time_graph(torch, g, n, warmup_replays=1, reps=3, warm=None, keep=None):
+    """Median ms per iteration over reps timed replays of the graph g (n iterations each),
+    each right after an untimed replay of `warm` (default g); synchronised before and after
+    every trial. Before the first trial, warm is replayed at least warmup_replays times and
+    for at least WARM_S seconds: from idle the GPU needs a few hundred ms of work to reach
+    its steady clocks (measured: LM head NB=1 trials of 20 steps at 36.8-40.5 us after one
+    warm-up replay, 35.8-36.4 us after 0.3 s). The per-replay figures go to keep.trials when
+    keep is given."""
+    warm = warm or g
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup_replays or time.perf_counter() - t0 < WARM_S:
+        warm.replay()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm.replay()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / n)
+    if keep is not None:
+        keep.trials = ts
+    return statistics.median(ts)
+
+
+def probe_lib():
+    """libq4mv_probe.so (reference kernels for measurement), with argument types set."""
+    import ctypes
+    path = os.path.join(ROOT, "affine_q4_gemv_amd", "libq4mv_probe.so")
+    L = ctypes.CDLL(path)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.q4mv_probe_read.argtypes = [p, i64, p, i32, p]
+    L.q4mv_probe_read.restype = i32
+    L.q4mv_probe_sink_words.argtypes = [i32]
+    L.q4mv_probe_sink_words.restype = i64
+    L.q4mv_probe_empty.argtypes = [i32, p]
+    L.q4mv_probe_empty.restype = i32
+    return L
+
+
+def _capture(torch, body, n):
+    """A HIP graph of n calls body(i) on a side stream (after two eager warm-up calls)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(2):
+            body(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            body(i)
+    return g
+
+
+def reference_legs(launches=200):
+    """The ceilings the GEMV figures are read against, timed like the GEMV (graphs of
+    back-to-back launches): a streaming read of each workload's weight bytes over rotated
+    copies at 1, 2, 4 and 8 blocks per CU, and the empty-kernel launch floor."""
+    import torch
+    L = probe_lib()
+    import workloads
+    out = []
+
+    def stream():
+        return torch.cuda.current_stream().cuda_stream
+
+    for name in ("lm_head", "up", "moe_down", "dense", "tiny"):
+        w = workloads.WORKLOADS[name]
+        nbytes = workloads.weight_bytes(w["n_mat"], w["out_dim"], w["in_dim"])
+        nbytes = (nbytes + 15) // 16 * 16
+        # (a graph of `launches` launches reads at most that many copies)
+        R = min(launches, max(1, math.ceil(ROTATE_BYTES / nbytes)))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251)
+                for i in range(R)]
+        res = {}
+        for bpc in (1, 2, 4, 8):
+            sink = torch.empty(L.q4mv_probe_sink_words(bpc), dtype=torch.int32, device="cuda")
+
+            def body(i, bpc=bpc, sink=sink):
+                st = L.q4mv_probe_read(bufs[i % R].data_ptr(), nbytes, sink.data_ptr(), bpc,
+                                       stream())
+                if st != 0:
+                    raise RuntimeError(f"q4mv_probe_read: status {st}")
+            g = _capture(torch, body, launches)
+            res[bpc] = time_graph(torch, g, launches, reps=5) * 1e3
+            del g, sink
+        best = min(res, key=res.get)
+        out.append({"leg": "streaming read (q4mv_probe_read)", "workload": name,
+                    "bytes": nbytes, "rotation_copies": R,
+                    "us_by_blocks_per_cu": {str(k): round(v, 3) for k, v in res.items()},
+                    "best_us": round(res[best], 3), "best_blocks_per_cu": best,
+                    "GBps": round(nbytes / (res[best] * 1e-6) / 1e9, 1),
+                    "pct_hbm_peak": round(100 * nbytes / (res[best] * 1e-6) / 1e9
+                                          / HBM_PEAK_GBPS, 1)})
+        del bufs
+        torch.cuda.empty_cache()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for blocks in (1, 2 * cus):
+        def body(i, blocks=blocks):
+            st = L.q4mv_probe_empty(blocks, stream())
+            if st != 0:
+                raise RuntimeError(f"q4mv_probe_empty: status {st}")
+        g = _capture(torch, body, launches)
+        us = time_graph(torch, g, launches, reps=5) * 1e3
+        out.append({"leg": "empty kernel (q4mv_probe_empty)", "blocks": blocks,
+                    "us_per_launch": round(us, 3)})
+    return out
+
+
 def cpu_baseline(name, nb, budget_s=10.0):
     """The CPU oracle on the full workload, repeated for about budget_s seconds (at least
     three passes); the median pass time gives the rate."""
@@ -559,14 +668,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": f"{args.workload} {prob.n_mat}x{prob.out_dim}x{prob.in_dim} "
                                f"affine-Q4 group 64, NB={prob.nb}",
                    "n_mat": prob.n_mat, "out_dim": prob.out_dim, "in_dim": prob.in_dim,
                    "nb": prob.nb, "group": 64, "weight_bytes": prob.weight_bytes,
                    "rotation_copies": prob.R, "seed": 0, "graph_captured": not args.eager,
-                   "operands": "u4 codes, bf16 scale+bias per 64, f16 activations, f32 acc",
+                   "warmup_note": f"at least {args.warmup} steps and {WARM_S} s of untimed "
+                                  "replays before the first timed trial",
+                   "operands": "u4 codes times f16 activations (f16 dot products and "
+                               "matrix-core products), f32 accumulation, bf16 scale+bias per 64",
                    "step": "q4mv_fused (activation prep inside the GEMV launch)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "rows_per_s": round(prob.n_mat * prob.out_dim / (step_ms * 1e-3), 1),
@@ -636,13 +748,18 @@ def main():
                               "rows_per_s": round(p.n_mat * p.out_dim / (ms * 1e-3), 1)})
                 del p
                 torch.cuda.empty_cache()
-        p = Problem("moe_down", 2)
-        ms = p.time_kernel(200)
-        gbps = p.weight_bytes / (ms * 1e-3) / 1e9
-        sweep.append({"workload": "moe_down", "nb": 2, "codes": "Q4",
-                      "kernel_us": round(ms * 1e3, 3), "weight_GBps": round(gbps, 1),
-                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1), "path": p.path})
-        del p
+        # the page's two-row claim at its shape: the 640-wide expert down projection (8
+        # experts x 2560 x 640) on the one-row, two-row and MFMA kernels, fused launches
+        for nb in (1, 2, 4):
+            p = Problem("moe_down", nb)
+            t = {path: p.time_path(path) * 1e3 for path in (1, 2, 3)}
+            sweep.append({"workload": "moe_down", "nb": nb, "compare": "kernel paths",
+                          "one_row_us": round(t[1], 3), "two_row_us": round(t[2], 3),
+                          "mfma_us": round(t[3], 3),
+                          "two_row_vs_one_row": round(t[1] / t[2] - 1.0, 3),
+                          "auto_path": p.path})
+            del p
+            torch.cuda.empty_cache()
         # the quantiser (off the GEMV path): dense f32 LM-head weights -> packed affine-Q4
         wf = torch.randn(151936, 2560, device="cuda") * 0.02
         q4 = __import__("affine_q4_gemv_amd")
@@ -690,6 +807,7 @@ def main():
                           "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)})
             del p
             torch.cuda.empty_cache()
+        sweep += reference_legs()
         result["sweep"] = sweep
 
     if not args.no_cpu:

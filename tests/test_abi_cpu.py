@@ -265,3 +265,42 @@ def test_experts_fused_validation(L):
     assert L.q4mv_experts_fused(*args(swiglu=2)) == EVALUE
     assert L.q4mv_experts_fused(*args(path=5)) == EPATH
     assert L.q4mv_experts_fused(*args(out=7, path=2)) == EODD
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "q4mv_probe.h")
+
+
+@pytest.fixture(scope="module")
+def P():
+    import ctypes
+    path = os.path.join(ROOT, "affine_q4_gemv_amd", "libq4mv_probe.so")
+    if not os.path.exists(path):
+        from affine_q4_gemv_amd import build
+        build.build()
+    L = ctypes.CDLL(path)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.q4mv_probe_read.argtypes = [p, i64, p, i32, p]
+    L.q4mv_probe_sink_words.argtypes = [i32]
+    L.q4mv_probe_sink_words.restype = i64
+    L.q4mv_probe_empty.argtypes = [i32, p]
+    return L
+
+
+def test_probe_exports_and_validation(P):
+    """The measurement library exports what its header declares and rejects bad arguments
+    before launching."""
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q4mv_probe\w*)\s*\(", text, re.M)
+    assert sorted(names) == ["q4mv_probe_empty", "q4mv_probe_read", "q4mv_probe_sink_words"]
+    for n in names:
+        assert hasattr(P, n)
+    assert P.q4mv_probe_read(None, 64, A, 2, None) == ENULL
+    assert P.q4mv_probe_read(A, 64, None, 2, None) == ENULL
+    for nbytes, bpc in ((0, 2), (40, 2), (64, 0), (64, 17)):
+        assert P.q4mv_probe_read(A, nbytes, A, bpc, None) == ESHAPE
+    assert P.q4mv_probe_read(A + 8, 64, A, 2, None) == EALIGN
+    assert P.q4mv_probe_read(A, 64, A + 2, 2, None) == EALIGN
+    assert P.q4mv_probe_sink_words(0) == ESHAPE and P.q4mv_probe_sink_words(17) == ESHAPE
+    assert P.q4mv_probe_sink_words(2) % 512 == 0
+    assert P.q4mv_probe_empty(0, None) == ESHAPE
+    assert P.q4mv_probe_empty((1 << 20) + 1, None) == ESHAPE
