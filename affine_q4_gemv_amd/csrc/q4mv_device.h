@@ -89,6 +89,57 @@ __device__ __forceinline__ uint4 make_pairs(uint2 e, uint2 o)
     return p;
 }
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// Packed maximum of two pairs of u16 (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pkmax_u16(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                   __builtin_bit_cast(u16x2_t, b)));
+}
+
+// One 8-column word x0..x7 of f32 activations, as the prep forms it: every value rounded to
+// f16 (nearest even), the four consecutive pairs summed in f32 ((float)a + (float)b), and
+// those sums added as (s01 + s23) + (s45 + s67). (A v_dot2_f32_f16 against (1, 1) is not a
+// substitute for the pair sum: it measured different bits from the f32 addition on pairs
+// whose sum must be rounded.) Returns the word in the pair layout
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7), the word's sum, and the packed maximum of the f16
+// magnitudes' bit patterns (halves: the even and the odd columns).
+struct XWord {
+    uint4 p;
+    float sum;
+    uint32_t mag;
+};
+__device__ __forceinline__ XWord x_word(const float (&f)[8])
+{
+    uint32_t q[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+        q[t] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)f[2 * t], (_Float16)f[2 * t + 1]});
+    float ps[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const half2_t h = __builtin_bit_cast(half2_t, q[t]);
+        ps[t] = (float)h[0] + (float)h[1];
+    }
+    XWord w;
+    w.sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // bytes of q[0] (x0,x1), q[1] (x2,x3), q[2] (x4,x5), q[3] (x6,x7)
+    w.p.x = __builtin_amdgcn_perm(q[2], q[0], 0x05040100u);  // (x0, x4)
+    w.p.y = __builtin_amdgcn_perm(q[2], q[0], 0x07060302u);  // (x1, x5)
+    w.p.z = __builtin_amdgcn_perm(q[3], q[1], 0x05040100u);  // (x2, x6)
+    w.p.w = __builtin_amdgcn_perm(q[3], q[1], 0x07060302u);  // (x3, x7)
+    w.mag = pkmax_u16(pkmax_u16(q[0] & 0x7FFF7FFFu, q[1] & 0x7FFF7FFFu),
+                      pkmax_u16(q[2] & 0x7FFF7FFFu, q[3] & 0x7FFF7FFFu));
+    return w;
+}
+
+// Whether a packed maximum of f16 magnitude patterns reaches 4096 (or is NaN / inf).
+__device__ __forceinline__ int mag_big(uint32_t m)
+{
+    return (int)((m & 0xFFFFu) >= 0x6C00u) | (int)((m >> 16) >= 0x6C00u);
+}
+
 // silu(g) * u in f32 (fn_moe_act_b, Constant BATCH_MSL page): g / (1 + e^-g) * u, with the
 // product rounded to f32 before any later conversion. The empty asm keeps the compiler from
 // merging the product with a following f32 -> f16 conversion into one mixed-precision FMA

@@ -186,100 +186,199 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // quad of lanes is one chunk, 8 lanes one group (words per row are a multiple of 8). With
     // xf_glu the rows are [gate | up] and the values silu(gate) * up (as q4mv_swiglu_prep
     // forms them). Returns whether this thread saw an |x| of 4096 or more.
-    auto fstage = [&](bool up) {
+    // Thread t takes words (units) t, t + TH, t + 2 TH, ... of the nb * in_dim / 8 staged
+    // words; their row and column are advanced incrementally (no division per word). The
+    // staging runs after each wave has issued its first weight loads, in rounds (2 words per
+    // thread with f32 activations, 4 units with the prepared ones); the next round's loads
+    // are issued before the current round is converted and written. (Issuing the first
+    // rounds ahead of the weight loads measured slower: the registers they hold across those
+    // loads cost the LM head its second block per CU.)
+    const int wrow = in_dim >> 3, words = nb * wrow;
+    const int dr = TH / wrow, dk = TH - dr * wrow;  // advance by TH words
+    auto adv = [&](int &r, int &kw) __attribute__((always_inline)) {
+        r += dr;
+        kw += dk;
+        if (kw >= wrow) {
+            kw -= wrow;
+            r++;
+        }
+    };
+    // Fused prep (xf non-null: f32 activations): the f16 rounding and the chunk sums of
+    // q4mv_prepare_x done here with the same additions (pair sums, a balanced tree over a
+    // chunk's 16 pairs: each thread adds its word's four pairs, two quad DPP steps add the
+    // chunk's four words; then a group's two chunks in order), so the LDS contents are
+    // bitwise those staged from q4mv_prepare_x's outputs. A quad of lanes is one chunk, 8
+    // lanes one group (words per row are a multiple of 8). With xf_glu the rows are
+    // [gate | up] and the values silu(gate) * up (as q4mv_swiglu_prep forms them). Returns
+    // whether this thread saw an |x| of 4096 or more.
+    auto fstage = [&](bool up) __attribute__((always_inline)) {
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
         const int rs4 = xf_glu ? in_full >> 1 : in_full >> 2;  // float4 per row
         const float4 *xf_m = reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4;
-        const int wrow = in_dim >> 3, words = nb * wrow;
         float *xsw = reinterpret_cast<float *>(xsg_w);
         const half2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
         const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
         const float sum_scale = up ? kTwoM20 : kTwoM24;
-        int big = 0;
-        for (int base = threadIdx.x; base < words; base += 2 * TH) {
-            float4 v[2][4];
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int wi = min(base + i * TH, words - 1);
-                const int r = wi / wrow;
-                xword_load(xf_m + (size_t)r * rs4, (k0 >> 3) + wi - r * wrow, in_full, xf_glu,
-                           v[i]);
+        uint32_t mag = 0;
+        // one word: f16 values, chunk sum (a quad of lanes is a chunk) and group sum (8
+        // lanes), and its LDS unit r*RS + 4c + j = the pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+        // scaled for the staging
+        auto fword = [&](int r, int kw, const float (&f)[8]) __attribute__((always_inline)) {
+            const XWord xw = x_word(f);
+            mag = pkmax_u16(mag, xw.mag);
+            float sum = xw.sum;
+            sum += dpp<0xB1>(sum);
+            sum += dpp<0x4E>(sum);
+            const float other = __shfl_xor(sum, 4, 64);  // the group's other chunk
+            if ((kw & 7) == 0) xsw[(kw >> 3) * 16 + r] = (sum + other) * sum_scale;
+            uint4 u = xw.p;
+            if (up) {
+                u.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, u.x) * sixteen);
+                u.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, u.z) * sixteen);
+            } else {
+                u.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, u.y) * sixteenth);
+                u.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, u.w) * sixteenth);
             }
+            lds[r * RS + kw] = u;
+        };
+        if (xf_glu) {
+            // [gate | up] rows: one word per thread at a time
+            for (int wi = threadIdx.x; wi < words; wi += TH) {  // uniform per 8 lanes
+                const int r = wi / wrow, kw = wi - r * wrow;
+                float4 v[4];
+                xword_load(xf_m + (size_t)r * rs4, (k0 >> 3) + kw, in_full, 1, v);
+                float f[8];
+                xword_values(v, 1, f);
+                fword(r, kw, f);
+            }
+        } else {
+            // plain rows: rounds of 2 words per thread, the next round's loads in flight
+            // while the current one is written
+            auto fload = [&](const int (&r)[2], const int (&kw)[2], float4 (&v)[2][2])
+                __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int wi = base + i * TH;
-                if (wi < words) {  // uniform per 8 lanes
-                    const int r = wi / wrow, kw = wi - r * wrow;
-                    float f[8];
-                    xword_values(v[i], xf_glu, f);
-                    _Float16 h[8];
-#pragma unroll
-                    for (int t = 0; t < 8; t++) h[t] = (_Float16)f[t];
-                    float ps[4];
-#pragma unroll
-                    for (int q = 0; q < 4; q++) ps[q] = (float)h[2 * q] + (float)h[2 * q + 1];
-                    float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                    sum += dpp<0xB1>(sum);
-                    sum += dpp<0x4E>(sum);
-                    const float other = __shfl_xor(sum, 4, 64);  // the group's other chunk
-                    if ((kw & 7) == 0) xsw[(kw >> 3) * 16 + r] = (sum + other) * sum_scale;
-                    // unit r*RS + 4c + j: the pairs (x0, x4) (x1, x5) (x2, x6) (x3, x7)
-                    const half2_t p0 = {h[0], h[4]}, p1 = {h[1], h[5]}, p2 = {h[2], h[6]},
-                                  p3 = {h[3], h[7]};
-                    big |= f16x2_big(p0) | f16x2_big(p1) | f16x2_big(p2) | f16x2_big(p3);
-                    uint4 u;
-                    u.x = __builtin_bit_cast(uint32_t, up ? p0 * sixteen : p0);
-                    u.y = __builtin_bit_cast(uint32_t, up ? p1 : p1 * sixteenth);
-                    u.z = __builtin_bit_cast(uint32_t, up ? p2 * sixteen : p2);
-                    u.w = __builtin_bit_cast(uint32_t, up ? p3 : p3 * sixteenth);
-                    lds[r * RS + kw] = u;
+                for (int i = 0; i < 2; i++) {
+                    const float4 *row = xf_m + (size_t)min(r[i], nb - 1) * rs4;
+                    v[i][0] = row[2 * ((k0 >> 3) + kw[i])];
+                    v[i][1] = row[2 * ((k0 >> 3) + kw[i]) + 1];
                 }
+            };
+            auto fput = [&](const int (&r)[2], const int (&kw)[2], const float4 (&v)[2][2])
+                __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    if (r[i] < nb) {  // uniform per 8 lanes
+                        const float f[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w,
+                                            v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
+                        fword(r[i], kw[i], f);
+                    }
+                }
+            };
+            auto next = [&](const int (&r)[2], const int (&kw)[2], int (&rn)[2], int (&kn)[2])
+                __attribute__((always_inline)) {
+                rn[0] = r[1];
+                kn[0] = kw[1];
+                adv(rn[0], kn[0]);
+                rn[1] = rn[0];
+                kn[1] = kn[0];
+                adv(rn[1], kn[1]);
+            };
+            float4 va[2][2], vb[2][2];
+            int ra[2], ka[2], rb[2], kb2[2];
+            ra[0] = threadIdx.x / wrow;
+            ka[0] = threadIdx.x - ra[0] * wrow;
+            ra[1] = ra[0];
+            ka[1] = ka[0];
+            adv(ra[1], ka[1]);
+            if (ra[0] < nb) fload(ra, ka, va);
+            while (ra[0] < nb) {
+                next(ra, ka, rb, kb2);
+                if (rb[0] < nb) fload(rb, kb2, vb);
+                fput(ra, ka, va);
+                if (rb[0] >= nb) break;
+                next(rb, kb2, ra, ka);
+                if (ra[0] < nb) fload(ra, ka, va);
+                fput(rb, kb2, vb);
             }
         }
         for (int u = threadIdx.x; u < groups * 16; u += TH)
             if ((u & 15) >= nb) xsw[u] = 0.0f;
-        return big;
+        return mag_big(mag);
     };
-    // the same from q4mv_prepare_x's outputs (xf null)
-    auto pstage = [&](bool up) {
+    // the same from q4mv_prepare_x's outputs (xf null): unit (r, 4c + j) from the even and odd
+    // streams, rounds of 4 units per thread
+    auto pstage = [&](bool up) __attribute__((always_inline)) {
         const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
         const uint2 *xe_m = xe + xrow0 * words8 + (k0 >> 3);
         const uint2 *xo_m = xo + xrow0 * words8 + (k0 >> 3);
         const float *xsum_m = xsum + xrow0 * Cf + kc0;
-        const int units = nb * C * 4;  // one per (row, chunk, word)
         const half2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
         const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
         const float sum_scale = up ? kTwoM20 : kTwoM24;
-        int big = 0;
-        // each round issues all of its loads before any LDS write: one memory round trip
-        for (int base = threadIdx.x; base < units; base += 4 * TH) {
-            uint2 e[4], o[4];
+        uint32_t mag = 0;
+        struct PRound { uint2 e[4], o[4]; int r[4], kw[4]; };
+        auto ppos = [&](PRound &p, int r, int kw) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int u = min(base + i * TH, units - 1);
-                const int r = u / (C * 4), cw = u - r * (C * 4);  // cw = 4c + j
-                const size_t at = (size_t)r * words8 + cw;
-                e[i] = xe_m[at];
-                o[i] = xo_m[at];
+                p.r[i] = r;
+                p.kw[i] = kw;
+                adv(r, kw);
             }
+        };
+        auto pload = [&](PRound &p) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int u = base + i * TH;
-                if (u < units) {
-                    const int r = u / (C * 4), cw = u - r * (C * 4);
-                    uint4 pr = make_pairs(e[i], o[i]);
-                    const half2_t p0 = __builtin_bit_cast(half2_t, pr.x);
-                    const half2_t p1 = __builtin_bit_cast(half2_t, pr.y);
-                    const half2_t p2 = __builtin_bit_cast(half2_t, pr.z);
-                    const half2_t p3 = __builtin_bit_cast(half2_t, pr.w);
-                    big |= f16x2_big(p0) | f16x2_big(p1) | f16x2_big(p2) | f16x2_big(p3);
-                    pr.x = __builtin_bit_cast(uint32_t, up ? p0 * sixteen : p0);
-                    pr.y = __builtin_bit_cast(uint32_t, up ? p1 : p1 * sixteenth);
-                    pr.z = __builtin_bit_cast(uint32_t, up ? p2 * sixteen : p2);
-                    pr.w = __builtin_bit_cast(uint32_t, up ? p3 : p3 * sixteenth);
-                    lds[r * RS + cw] = pr;
+                const size_t at = (size_t)min(p.r[i], nb - 1) * words8 + p.kw[i];
+                p.e[i] = xe_m[at];
+                p.o[i] = xo_m[at];
+            }
+        };
+        auto pput = [&](const PRound &p) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if (p.r[i] < nb) {
+                    uint4 pr = make_pairs(p.e[i], p.o[i]);
+                    mag = pkmax_u16(mag, pkmax_u16(pkmax_u16(p.e[i].x & 0x7FFF7FFFu,
+                                                              p.e[i].y & 0x7FFF7FFFu),
+                                                    pkmax_u16(p.o[i].x & 0x7FFF7FFFu,
+                                                              p.o[i].y & 0x7FFF7FFFu)));
+                    if (up) {
+                        pr.x = __builtin_bit_cast(uint32_t,
+                                                  __builtin_bit_cast(half2_t, pr.x) * sixteen);
+                        pr.z = __builtin_bit_cast(uint32_t,
+                                                  __builtin_bit_cast(half2_t, pr.z) * sixteen);
+                    } else {
+                        pr.y = __builtin_bit_cast(uint32_t,
+                                                  __builtin_bit_cast(half2_t, pr.y) * sixteenth);
+                        pr.w = __builtin_bit_cast(uint32_t,
+                                                  __builtin_bit_cast(half2_t, pr.w) * sixteenth);
+                    }
+                    lds[p.r[i] * RS + p.kw[i]] = pr;
                 }
             }
+        };
+        PRound pa, pb;
+        {
+            const int r0 = threadIdx.x / wrow;
+            ppos(pa, r0, threadIdx.x - r0 * wrow);
+        }
+        if (pa.r[0] < nb) pload(pa);
+        while (pa.r[0] < nb) {
+            {
+                int r = pa.r[3], kw = pa.kw[3];
+                adv(r, kw);
+                ppos(pb, r, kw);
+            }
+            if (pb.r[0] < nb) pload(pb);
+            pput(pa);
+            if (pb.r[0] >= nb) break;
+            {
+                int r = pb.r[3], kw = pb.kw[3];
+                adv(r, kw);
+                ppos(pa, r, kw);
+            }
+            if (pa.r[0] < nb) pload(pa);
+            pput(pb);
         }
         float *xsw = reinterpret_cast<float *>(xsg_w);
         for (int u = threadIdx.x; u < groups * 16; u += TH) {
@@ -288,12 +387,12 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
             const float a = xsum_m[(size_t)rr * Cf + 2 * g], b = xsum_m[(size_t)rr * Cf + 2 * g + 1];
             xsw[u] = r < nb ? (a + b) * sum_scale : 0.0f;
         }
-        return big;
+        return mag_big(mag);
     };
     // stages with the x16 scale unless a staged |x| reaches 4096; returns the output scale.
     // Each wave writes its own vote (so nothing needs clearing first); after the barrier
     // every thread reads all of them.
-    auto stage = [&]() {
+    auto stage = [&]() __attribute__((always_inline)) {
         const int mine = __any(xf ? fstage(true) : pstage(true)) ? 1 : 0;
         if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = mine;
         __syncthreads();

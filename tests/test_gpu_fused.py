@@ -199,3 +199,27 @@ def test_fused_graph_replays():
         want_ye = q4.q4mv_experts_fused(d["w"], d["s"], d["b"], sel, gu, nb, False, swiglu=True)
         torch.cuda.synchronize()
         assert torch.equal(got_y, want_y) and torch.equal(got_ye, want_ye), f"replay {rep}"
+
+
+# Pair sums of f16 values that fall on f32 rounding ties (2048 + 2^-13 rounds down to even,
+# 2048 + 3 * 2^-13 up; the same at 4096, which also takes the MFMA kernel's fallback
+# staging) and signed zeros (-0 + -0 = -0): the fused staging's sums against the prep's.
+@pytest.mark.parametrize("big", [False, True], ids=["x16-staging", "fallback-staging"])
+def test_fused_pair_sum_ties(oracle_lib, big):
+    n_mat, out_dim, in_dim, nb = 1, 96, 512, 4
+    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=123)
+    x = case["x"].reshape(-1)
+    a = 4096.0 if big else 2048.0
+    ulp = a * 2.0 ** -23
+    pairs = [(a, ulp / 2), (a, 1.5 * ulp), (-a, -ulp / 2), (-a, -1.5 * ulp), (-0.0, -0.0),
+             (0.0, -0.0), (-0.0, 0.0), (ulp / 2, a)]
+    for k, (p, q) in enumerate(pairs):
+        for rep in range(4):  # several rows and chunks
+            at = 2 * k + 130 * rep * 4
+            x[at], x[at + 1] = p, q
+    x[256:288] = -0.0  # a whole chunk of negative zeros
+    d = upload(case)
+    check_paths(d, f"pair-sum ties big={big}", out_dim)
+    # an all-negative-zero chunk sums to -0 in the prep
+    xs = d["xsum"].cpu().numpy()
+    assert np.signbit(xs[0, 256 // 32]) and xs[0, 256 // 32] == 0.0
