@@ -76,6 +76,10 @@
 #ifndef Q4MV_MFMA_MF16
 #define Q4MV_MFMA_MF16 1
 #endif
+// Tile-block scale loads (SBW = 32) where they apply.
+#ifndef Q4MV_MFMA_TBS
+#define Q4MV_MFMA_TBS 1
+#endif
 #ifndef Q4MV_MFMA_BLOCKS_PER_CU
 #define Q4MV_MFMA_BLOCKS_PER_CU 4
 #endif
@@ -87,7 +91,12 @@ constexpr int kMfmaWaves = 8;
 // Per-wave LDS scratch of one unit: codes 32 rows x 128 B, then scales and biases
 // 2 x 32 rows x 8 B, or x 16 B with 16-byte scale loads (in 16-byte units).
 constexpr int kScratchUnits = 32 * 8 + 32;
-constexpr int scratch_units(int sbw) { return 32 * 8 + (sbw == 16 ? 64 : 32); }
+constexpr int scratch_units(int sbw) { return 32 * 8 + (sbw == 32 ? 0 : sbw == 16 ? 64 : 32); }
+// Tile-block scales (SBW = 32): each tile group keeps its tile's scales and biases (32 rows x
+// groups x 2 arrays of bf16) in an LDS buffer; a lane loads at most kTbPieces 16-byte pieces
+// of the next tile's block.
+constexpr int kTbPieces = 3;
+constexpr int kTbMaxGroups = 48;  // 8 * groups pieces <= 128 lanes x kTbPieces
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // A unit's scales and biases in flight: two dwords (one 8-byte load per lane) or four
 // 2-byte values (compact loads).
@@ -122,13 +131,20 @@ __device__ __forceinline__ u32x4 lowbit_to_q4(const u32x4 v)
 }
 
 // WPB: waves per block. KS: waves per tile (K-split). NB16: activation rows 8..15 are live
-// (nb > 8). SBW: how a lane loads its row's scales (lanes 0..31) or biases (32..63):
+// (nb > 8; with MF16 the code is the same, the instance separate). Tile-block MF16 kernels for
+// nb <= 8 are held to 128 VGPRs (four waves per SIMD: two 8-wave blocks per CU). SBW: how the scales and biases are loaded: 32 = per tile, the tile's whole
+// block (its 32 rows' scales, then their biases: two contiguous runs of 64 * groups bytes)
+// read with coalesced 16-byte loads shared by the KS = 2 waves of the tile group, one tile
+// ahead, into a per-tile-group LDS buffer (groups % 8 == 0, at most kTbMaxGroups, whole rows,
+// 16-byte aligned arrays; in a read-only probe of the LM head's access pattern the scattered
+// loads below cost 8 us beyond the codes and this one 4.3 us); else per unit, lanes 0..31 a
+// row's scales and lanes 32..63 its biases:
 // 16 = one aligned 16-byte load for two quads, made by the unit of the even quad (or the
 // first unit of a part) and kept in the scratch for the next (groups % 8 == 0, 16-byte
 // aligned arrays; halves the scattered scale loads); 8 = one aligned 8-byte load per quad
 // (groups % 4 == 0, 8-byte aligned); 2 = four 2-byte loads with clamped indices.
 template <int WPB, int KS, bool NB16, int SBW, bool MF16, int BITS = 4>
-__global__ __launch_bounds__(WPB * 64) void mfma_kernel(
+__global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
@@ -490,7 +506,9 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 #endif
         }
         const uint16_t *srow = sb_m + (size_t)(trow + sbrow) * gf;
-        if constexpr (SBW == 16) {
+        if constexpr (SBW == 32) {
+            (void)srow;  // the tile's block is in LDS
+        } else if constexpr (SBW == 16) {
             // only units that start a pair load (measured faster than a dummy load)
             if ((qd & 1) == 0 || u == 0) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(srow + 4 * (qd & ~1));
@@ -516,6 +534,37 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     // then scales of rows 0..31 and biases of rows 0..31 as 8-byte (16-byte) entries.
     uint4 *const scratch = scratch_all + wv * scratch_units(SBW);
     uint2 *const sbs = reinterpret_cast<uint2 *>(scratch + 32 * 8);
+    // tile-block scales: this tile group's buffer, scales [32][groups] then biases, bf16
+    uint4 *const tbuf = scratch_all + WPB * scratch_units(SBW) + slot * 8 * groups;
+    const uint16_t *const tbs = reinterpret_cast<const uint16_t *>(tbuf);
+    uint4 tb0 = {0u, 0u, 0u, 0u}, tb1 = tb0, tb2 = tb0;  // kTbPieces pieces in flight
+    // the block of `tile` into registers: lane l of wave `quarter` takes pieces
+    // 64 * quarter + l + 128 i of the 8 * groups (scales, then biases)
+    auto tb_load = [&](int tile) __attribute__((always_inline)) {
+        if constexpr (SBW == 32) {
+            const size_t trow = (size_t)tile_row(min(tile, tiles - 1)) * groups;
+            const uint4 *sp = reinterpret_cast<const uint4 *>(s_m + trow);
+            const uint4 *bp = reinterpret_cast<const uint4 *>(b_m + trow);
+            // every load is made (pieces past the block re-read its last piece), so the
+            // registers stay registers and the loads stay in flight
+            auto piece = [&](int i) __attribute__((always_inline)) {
+                const int pc = min(64 * quarter + lane + 128 * i, 8 * groups - 1);
+                return *(pc < 4 * groups ? sp + pc : bp + (pc - 4 * groups));
+            };
+            static_assert(kTbPieces == 3, "three pieces per lane");
+            tb0 = piece(0);
+            tb1 = piece(1);
+            tb2 = piece(2);
+        }
+    };
+    auto tb_store = [&]() __attribute__((always_inline)) {
+        if constexpr (SBW == 32) {
+            const int pc = 64 * quarter + lane;
+            if (pc < 8 * groups) tbuf[pc] = tb0;
+            if (pc + 128 < 8 * groups) tbuf[pc + 128] = tb1;
+            if (pc + 256 < 8 * groups) tbuf[pc + 256] = tb2;
+        }
+    };
     auto put = [&](const u32x4 (&cw)[4], const SbRegs &sb, int qd, int u) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -526,7 +575,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
         if constexpr (SBW == 16) {
             if ((qd & 1) == 0 || u == 0)
                 reinterpret_cast<uint4 *>(sbs)[lane] = uint4{sb.v[0], sb.v[1], sb.v[2], sb.v[3]};
-        } else {
+        } else if constexpr (SBW != 32) {
             sbs[lane] = uint2{sb.v[0], sb.v[1]};
         }
     };
@@ -567,10 +616,13 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
     };
     u32x4 c0[4], c1[4];
     SbRegs s0, s1;
+    // the first tile's scale block (visible to the tile group after the staging barrier)
+    tb_load(base + slot);  // (a tile past the end re-reads the last one: unused)
     if (more(abase)) load(abase + slot, unit_quad(aui), aui, c0, s0);
     advance(abase, aui);
     if (more(abase)) load(abase + slot, unit_quad(aui), aui, c1, s1);
     advance(abase, aui);
+    if (more(base)) tb_store();
     const float yscale = stage();  // every wave joins the staging barriers
     if (!more(base)) return;
     auto step_unit = [&](u32x4 (&cc)[4], SbRegs &sb) {
@@ -584,6 +636,8 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
         if (ui == 0) {
 #pragma unroll
             for (int i = 0; i < NACC; i++) acc[i] = 0.0f;
+            // the next tile's scale block, in flight during this tile
+            tb_load(base + tstride + slot);
         }
         if constexpr (MF16) {
             // scales and biases of this lane's two output rows (one per 16-row half)
@@ -591,8 +645,13 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
 #pragma unroll
             for (int t = 0; t < 2; t++) {
                 const int row = 16 * t + n16;
-                s4[t] = SBW == 16 ? sbs[2 * row + (qx & 1)] : sbs[row];
-                b4[t] = SBW == 16 ? sbs[2 * (32 + row) + (qx & 1)] : sbs[32 + row];
+                if constexpr (SBW == 32) {
+                    s4[t] = *reinterpret_cast<const uint2 *>(tbs + row * groups + 4 * qx);
+                    b4[t] = *reinterpret_cast<const uint2 *>(tbs + (32 + row) * groups + 4 * qx);
+                } else {
+                    s4[t] = SBW == 16 ? sbs[2 * row + (qx & 1)] : sbs[row];
+                    b4[t] = SBW == 16 ? sbs[2 * (32 + row) + (qx & 1)] : sbs[32 + row];
+                }
             }
 #pragma unroll
             for (int g4 = 0; g4 < 4; g4++) {
@@ -635,8 +694,11 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                 }
             }
         } else {
-            const uint2 s4 = SBW == 16 ? sbs[2 * n + (qx & 1)] : sbs[n];
-            const uint2 b4 = SBW == 16 ? sbs[2 * (32 + n) + (qx & 1)] : sbs[32 + n];
+            const uint2 s4 = SBW == 32   ? *reinterpret_cast<const uint2 *>(tbs + n * groups + 4 * qx)
+                             : SBW == 16 ? sbs[2 * n + (qx & 1)] : sbs[n];
+            const uint2 b4 = SBW == 32
+                                 ? *reinterpret_cast<const uint2 *>(tbs + (32 + n) * groups + 4 * qx)
+                             : SBW == 16 ? sbs[2 * (32 + n) + (qx & 1)] : sbs[32 + n];
     #pragma unroll
             for (int g4 = 0; g4 < 4; g4++) {
                 const int g = 4 * qx + g4;
@@ -712,6 +774,12 @@ __global__ __launch_bounds__(WPB * 64) void mfma_kernel(
                 }
             }
             step++;
+            // every wave of the block has read this tile's scale block (the combine barrier
+            // above): the next one replaces it, and is visible after the second barrier
+            if constexpr (SBW == 32) {
+                if (more(base + tstride)) tb_store();
+                __syncthreads();
+            }
         }
         advance(base, ui);
         return more(base);
@@ -732,6 +800,8 @@ static bool use_mf16(int ks, int nb, long tiles)
 template <int WPB, int KS, bool NB16, bool MF16>
 static MfmaFn pick_sb(int sbw)
 {
+    if constexpr (KS == 2 && WPB == kMfmaWaves)
+        if (sbw == 32) return mfma_kernel<WPB, KS, NB16, 32, MF16>;
     return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16, MF16>
            : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8, MF16>
                       : mfma_kernel<WPB, KS, NB16, 2, MF16>;
@@ -741,6 +811,11 @@ static MfmaFn pick_sb(int sbw)
 template <int BITS, int KS>
 static MfmaFn pick_lowbit_ks(bool nb16, int sbw, bool mf16)
 {
+    if constexpr (KS == 2)
+        if (sbw == 32)
+            return mf16   ? mfma_kernel<kMfmaWaves, KS, false, 32, true, BITS>
+                   : nb16 ? mfma_kernel<kMfmaWaves, KS, true, 32, false, BITS>
+                          : mfma_kernel<kMfmaWaves, KS, false, 32, false, BITS>;
     if constexpr (KS <= 2)
         if (mf16)
             return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, false, 16, true, BITS>
@@ -764,9 +839,12 @@ static MfmaFn pick_lowbit(int ks, bool nb16, int sbw, bool mf16)
 template <int WPB, int KS>
 static MfmaFn pick(bool nb16, int sbw, bool mf16)
 {
-    // the 16x16x32 path covers 16 activation rows either way
+    // the 16x16x32 path covers 16 activation rows either way; nb > 8 gets an instance of its
+    // own so that the register cap for two blocks per CU (tile-block scales, nb <= 8) does
+    // not apply where the LDS allows only one
     if constexpr (KS <= 2)
-        if (mf16) return pick_sb<WPB, KS, false, true>(sbw);
+        if (mf16)
+            return nb16 ? pick_sb<WPB, KS, true, true>(sbw) : pick_sb<WPB, KS, false, true>(sbw);
     return nb16 ? pick_sb<WPB, KS, true, false>(sbw) : pick_sb<WPB, KS, false, false>(sbw);
 }
 
@@ -843,7 +921,16 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
         g0 % 8 == 0 && (uintptr_t)a.scales % 16 == 0 && (uintptr_t)a.biases % 16 == 0 &&
         lds0 + (size_t)sh.wpb * scratch_units(16) * 16 <= kMaxLds)
         sbw = 16;
-    const size_t lds = lds0 + (size_t)sh.wpb * scratch_units(sbw) * 16;
+    // tile-block scales (K-split 2, whole rows of 8k groups, full tiles) where their LDS
+    // buffers fit next to the rest
+    const size_t tb_bytes = (size_t)(sh.wpb / std::max(1, sh.ks)) * 128 * groups;
+    if (Q4MV_MFMA_TBS && sh.ks == 2 && sh.wpb == kMfmaWaves && groups % 8 == 0 &&
+        groups <= kTbMaxGroups && klen == a.in_dim && a.out_dim >= 32 &&
+        (uintptr_t)a.scales % 16 == 0 && (uintptr_t)a.biases % 16 == 0 &&
+        lds0 + (size_t)sh.wpb * scratch_units(32) * 16 + tb_bytes <= kMaxLds)
+        sbw = 32;
+    const size_t lds =
+        lds0 + (size_t)sh.wpb * scratch_units(sbw) * 16 + (sbw == 32 ? tb_bytes : 0);
     MfmaFn fn;
     if (a.bits != 4) {
         if (sh.wpb != kMfmaWaves || sbw == 2) return hipErrorInvalidValue;  // checked on the host
