@@ -512,8 +512,10 @@ def _read_csv_rows(run_dir, suffix):
 
 
 def summarize_trace(run_dir, out, cmd, bench_log=None):
-    """Kernel statistics of a rocprofv3 --kernel-trace --stats run, plus the GEMV kernel
-    duration bench.py measured with HIP events in the same run (from its JSON line)."""
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run, the GEMV kernel's
+    per-dispatch durations from the same trace (all dispatches, and the last 1000: steady-state
+    graph replays at the end of a bench.py run), and the GEMV kernel time bench.py measured
+    with HIP events in the same run (from its JSON line)."""
     rows = _read_csv_rows(run_dir, "kernel_stats.csv")
     if not rows:
         raise SystemExit(f"no kernel_stats.csv under {run_dir}")
@@ -524,15 +526,28 @@ def summarize_trace(run_dir, out, cmd, bench_log=None):
         name = name[:name.index("(")] if "(" in name and not name.startswith("_Z") else name
         lines.append(f"{r.get('Calls')}, {r.get('TotalDurationNs')}, {r.get('AverageNs')}, "
                      f"{r.get('MinNs')}, {r.get('MaxNs')}, {r.get('Percentage')}, {name}")
+    res = None
     if bench_log:
         for line in open(bench_log):
             if line.startswith("{"):
                 res = json.loads(line)
-                gemv = [r for r in rows if res["roofline"]["kernel"] in r.get("Name", "")]
-                lines.append(f"# bench.py in the same run: {res['roofline']['kernel']} "
-                             f"{res['roofline']['kernel_us']} us per launch (HIP events); "
-                             f"rocprofv3 average "
-                             f"{float(gemv[0]['AverageNs']) / 1e3 if gemv else float('nan'):.3f} us")
+    if res:
+        kern = res["roofline"]["kernel"]
+        disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                      for r in _read_csv_rows(run_dir, "kernel_trace.csv")
+                      if kern in r.get("Kernel_Name", ""))
+        durs = [d for _, d in disp]
+        tail = durs[-1000:]
+        if durs:
+            lines.append(f"# {kern} dispatches in the trace: {len(durs)}, average "
+                         f"{statistics.mean(durs) / 1e3:.3f} us, median "
+                         f"{statistics.median(durs) / 1e3:.3f} us; last {len(tail)} (steady-state "
+                         f"replays): average {statistics.mean(tail) / 1e3:.3f} us, median "
+                         f"{statistics.median(tail) / 1e3:.3f} us")
+        lines.append(f"# bench.py in the same run: {kern} {res['roofline']['kernel_us']} us per "
+                     f"launch (HIP events around back-to-back launches, so launch gaps included), "
+                     f"{res['roofline']['achieved']} GB/s algorithmic, frac "
+                     f"{res['roofline']['frac']}, weight GB/s {res['value']}")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
