@@ -8,24 +8,33 @@
 
 namespace q4mv_impl {
 
-// nb up to this value runs on the VALU dot-product kernels on short launches, above it on
-// the MFMA kernel; from 2 rows the MFMA kernel already wins on matrices of at least
-// kMfmaMinTilesSmallNb 32-row tiles (measured crossovers on MI355X: LM head NB=2 MFMA 40.5 us
-// against 43.1 two-row and 46.2 one-row; 9728 x 2560 NB=2 one-row 7.8 us against 8.5 MFMA).
-constexpr int kValuAutoMaxNB = 3;
-constexpr long kMfmaMinTilesSmallNb = 1024;
+// The automatic choice between the VALU dot-product kernels and the MFMA kernel, by the
+// activation rows and the 32-row tiles of one matrix. The MFMA kernel costs more per launch
+// (it stages every activation row in LDS, and each of its units runs on a 32-row tile
+// whatever nb is), the VALU kernels more per activation row. Measured crossovers on MI355X
+// (graph-timed fused launches, us, one-row VALU against MFMA):
+//   2560 x 2560 (80 tiles)        nb 2: 5.2 / 7.0, nb 3: 6.0 / 7.2, nb 4: 6.9 / 7.6, nb 5: 9.9 / 7.9
+//   8 x 2560 x 640 (80 tiles)     nb 2: 6.1 / 7.3, nb 3: 6.7 / 7.4, nb 4: 7.5 / 7.6, nb 5: 8.7 / 7.6
+//   9728 x 2560 (304 tiles)       nb 2: 7.7 / 8.7, nb 3: 9.1 / 8.9, nb 4: 10.6 / 9.3
+//   151936 x 2560 (4748 tiles)    nb 2: 46.2 / 40.5, nb 3: 56.6 / 41.4
+// so: the MFMA kernel from nb 5; at nb 3 and 4 from 256 tiles; at nb 2 from 1024 tiles.
+constexpr int kValuAutoMaxNB = 4;
+constexpr long kMfmaMinTilesNb34 = 256;
+constexpr long kMfmaMinTilesNb2 = 1024;
 
-// The automatic choice, from (nb, out_dim) only: MFMA for larger batches (K-sliced where the
-// staged activations of a whole row do not fit in LDS), else one of the VALU kernels:
-// q4mv runs the one-row kernel (on MI355X as fast or faster than the two-row kernel at every
-// measured shape, the 640-wide expert down projection included) and q4mv_2row the two-row
-// kernel. The one-row and two-row kernels give bitwise the same result, so q4mv and q4mv_2row
-// agree whichever they take.
+// The automatic choice, from (nb, out_dim) only (the MFMA kernel runs K-sliced where the
+// staged activations of a whole row do not fit in LDS). On the VALU side q4mv runs the
+// one-row kernel (on MI355X as fast or faster than the two-row kernel at every measured
+// shape, the 640-wide expert down projection included) and q4mv_2row the two-row kernel.
+// The one-row and two-row kernels give bitwise the same result, so q4mv and q4mv_2row agree
+// whichever they take.
 int auto_path(int in_dim, int nb, bool two_row, int out_dim)
 {
     (void)in_dim;
     const long tiles = (out_dim + 31) / 32;
-    if (nb > kValuAutoMaxNB || (nb > 1 && tiles >= kMfmaMinTilesSmallNb)) return kMfma;
+    if (nb > kValuAutoMaxNB || (nb > 2 && tiles >= kMfmaMinTilesNb34) ||
+        (nb == 2 && tiles >= kMfmaMinTilesNb2))
+        return kMfma;
     return two_row ? kValu2 : kValu1;
 }
 
