@@ -67,11 +67,11 @@ int device_cus();
 // Largest dynamic LDS a block may use on gfx950.
 constexpr size_t kMaxLds = 160 * 1024;
 // LDS bytes of the MFMA kernel for a shape: staged f16 activations + per-group sums + the
-// per-wave staging votes (the partial-sum buffers of mfma_part_bytes come on top).
+// per-wave staging votes and a zero operand (the partial-sum buffers of mfma_part_bytes come on top).
 inline size_t mfma_lds_bytes(int in_dim, int nb)
 {
-    // nb rows of 4C + 1 pair units, then groups x 16 sums, then 8 ints
-    return (size_t)nb * (4 * (in_dim / 32) + 1) * 16 + (size_t)(in_dim / 64) * 16 * 4 + 32;
+    // nb rows of 4C + 1 pair units, then groups x 16 sums, then 8 ints and 32 zero bytes
+    return (size_t)nb * (4 * (in_dim / 32) + 1) * 16 + (size_t)(in_dim / 64) * 16 * 4 + 64;
 }
 // Partial-sum buffers of the MFMA kernel: 2 steps x tile groups per block x (ks - 1) parts
 // x lanes holding live rows x nacc accumulators.

@@ -76,6 +76,10 @@
 #ifndef Q4MV_MFMA_MF16
 #define Q4MV_MFMA_MF16 1
 #endif
+// The 16x16x32 shape for nb 5..8 as well (two 8-row group slots per accumulation).
+#ifndef Q4MV_MFMA_MF16_R8
+#define Q4MV_MFMA_MF16_R8 1
+#endif
 // Tile-block scale loads (SBW = 32) where they apply.
 #ifndef Q4MV_MFMA_TBS
 #define Q4MV_MFMA_TBS 1
@@ -143,8 +147,8 @@ __device__ __forceinline__ u32x4 lowbit_to_q4(const u32x4 v)
 // first unit of a part) and kept in the scratch for the next (groups % 8 == 0, 16-byte
 // aligned arrays; halves the scattered scale loads); 8 = one aligned 8-byte load per quad
 // (groups % 4 == 0, 8-byte aligned); 2 = four 2-byte loads with clamped indices.
-template <int WPB, int KS, bool NB16, int SBW, bool MF16, int BITS = 4>
-__global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) void mfma_kernel(
+template <int WPB, int KS, bool NB16, int SBW, bool MF16, int BITS = 4, bool R8 = false>
+__global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 : 1) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
     const uint2 *__restrict__ xo, const float *__restrict__ xsum, float *__restrict__ y,
@@ -176,9 +180,10 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) voi
     // the lanes that hold activation rows below nb).
     const int RS = 4 * C + 1;
     float4_t *const xsg_w = reinterpret_cast<float4_t *>(lds + nb * RS);
-    // one int per wave for the staging scale vote (32 bytes), then the partial sums
+    // one int per wave for the staging scale vote (32 bytes), two zero units (32 bytes: the
+    // A operand of rows outside their group slot), then the partial sums
     int *const vote = reinterpret_cast<int *>(xsg_w + groups * 4);
-    float *const part = reinterpret_cast<float *>(vote + 8);
+    float *const part = reinterpret_cast<float *>(vote + 16);
     // lanes whose accumulators hold activation rows below nb (16x16x32: rows 4kb .. 4kb+3)
     const int plan = MF16 ? 16 * ((nb + 3) >> 2) : 64;
     uint4 *const scratch_all =
@@ -409,6 +414,7 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) voi
     // Each wave writes its own vote (so nothing needs clearing first); after the barrier
     // every thread reads all of them.
     auto stage = [&]() __attribute__((always_inline)) {
+        if (threadIdx.x < 8) vote[8 + threadIdx.x] = 0;  // the zero units
         const int mine = __any(xf ? fstage(true) : pstage(true)) ? 1 : 0;
         if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = mine;
         __syncthreads();
@@ -581,8 +587,16 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) voi
     };
 
     // this lane's activation row in LDS (row nb - 1 past nb), offset to its chunk parity
-    const uint4 *const xrow =
-        MF16 ? lds + min(n16, nb - 1) * RS + 2 * kb : lds + min(n, nb - 1) * RS + 4 * h;
+    // 16x16x32 group slots: RG activation rows per slot (4 for nb <= 4, 8 for nb 5..8, 16
+    // above), NS slots, ND accumulations per unit and half; sa: the slot of this lane's A
+    // rows, kbd: the slot of its D rows
+    constexpr int RG = NB16 ? 16 : R8 ? 8 : 4;
+    constexpr int NS = 16 / RG, ND = 4 / NS;
+    const int sa = n16 / RG, kbd = kb / (RG / 4);
+    const uint4 *const xrow = MF16 ? lds + min(n16 % RG, nb - 1) * RS + 2 * kb
+                                   : lds + min(n, nb - 1) * RS + 4 * h;
+    // zeros for A rows outside their group's slot
+    const uint4 *const zrow = reinterpret_cast<const uint4 *>(vote + 8);
     float acc[NACC];
     // Low-bit codes reconstruct at the middle of the 4-bit range each stands for:
     // w = (4q + 1.5) s + b (Q2), (2q + 0.5) s + b (Q3); the fold takes K s and M s + b (formed
@@ -640,12 +654,22 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) voi
             tb_load(base + tstride + slot);
         }
         if constexpr (MF16) {
-            // scales and biases of this lane's two output rows (one per 16-row half)
+            // Group slots: the 16 A rows hold NS = 16 / RG slots of RG activation rows, and
+            // an A row of slot sl carries its activations only while group sl (mod NS) of
+            // the unit is multiplied (else it reads zeros), so D rows of slot sl accumulate
+            // that group alone: D_j (j < ND) takes groups j*NS .. j*NS+NS-1 of the unit.
+            // Lane (n16, kb) holds D rows 4kb .. 4kb+3 = slot kb / (RG/4), activation rows
+            // 4 (kb % (RG/4)) .. +3: one fold per lane, D and half covers NS groups.
+            // scales and biases of this lane's two output rows: the quad's four (one slot),
+            // or this lane's group in each D (several slots)
+            // (tile-block scales with several slots: read at the fold, one bf16 each)
             uint2 s4[2], b4[2];
 #pragma unroll
             for (int t = 0; t < 2; t++) {
                 const int row = 16 * t + n16;
-                if constexpr (SBW == 32) {
+                if constexpr (SBW == 32 && NS > 1) {
+                    (void)row;
+                } else if constexpr (SBW == 32) {
                     s4[t] = *reinterpret_cast<const uint2 *>(tbs + row * groups + 4 * qx);
                     b4[t] = *reinterpret_cast<const uint2 *>(tbs + (32 + row) * groups + 4 * qx);
                 } else {
@@ -653,44 +677,68 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) voi
                     b4[t] = SBW == 16 ? sbs[2 * (32 + row) + (qx & 1)] : sbs[32 + row];
                 }
             }
-#pragma unroll
-            for (int g4 = 0; g4 < 4; g4++) {
+            // scale and bias (f32) of this lane's group in D_j, output row 16t + n16
+            auto sb_of = [&](int t, int j, float &sj, float &bj) __attribute__((always_inline)) {
+                const int g4 = j * NS + kbd;
                 const int g = 4 * qx + g4;
                 const bool live = qd < q_end && g < groups;
-                const int gx = min(g, groups - 1);
-                const uint4 *xg = xrow + 8 * gx;
-                const half8_t a0 = __builtin_bit_cast(half8_t, xg[0]);
-                const half8_t a1 = __builtin_bit_cast(half8_t, xg[1]);
-                // D layout: lane (n16, kb), register v holds activation row 4kb + v
-                const float4_t xa4 = xsg[gx * 4 + kb];
-#pragma unroll
-                for (int t = 0; t < 2; t++) {
+                uint32_t sbits, bbits;
+                if constexpr (SBW == 32 && NS > 1) {
                     const int row = 16 * t + n16;
-                    // words 2kb, 2kb+1 of the group: chunk 2g4 + kb/2, bytes 8(kb%2) ..
-                    const uint2 bw = reinterpret_cast<const uint2 *>(
-                        scratch)[(row * 8 + ((2 * g4 + (kb >> 1)) ^ (row & 7))) * 2 + (kb & 1)];
-                    const uint32_t wd[2] = {bw.x, bw.y};
-                    float4_t d;
-#pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        const uint32_t w8 = wd[j] >> 8;
-                        const uint4 bq = {wd[j] & 0x000F000Fu, wd[j] & 0x00F000F0u,
-                                          w8 & 0x000F000Fu, w8 & 0x00F000F0u};
-                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            j == 0 ? a0 : a1, __builtin_bit_cast(half8_t, bq),
-                            j == 0 ? float4_t{} : d, 0, 0, 0);
-                    }
+                    const int gx = min(g, groups - 1);
+                    sbits = (uint32_t)tbs[row * groups + gx] << 16;
+                    bbits = (uint32_t)tbs[(32 + row) * groups + gx] << 16;
+                } else {
                     const uint32_t sw = (g4 < 2) ? s4[t].x : s4[t].y;
                     const uint32_t bwd = (g4 < 2) ? b4[t].x : b4[t].y;
-                    const uint32_t sbits = (g4 & 1) ? (sw & 0xFFFF0000u) : (sw << 16);
-                    const uint32_t bbits = (g4 & 1) ? (bwd & 0xFFFF0000u) : (bwd << 16);
-                    float s = __uint_as_float(live ? sbits : 0u);
-                    float b = __uint_as_float(live ? bbits : 0u);
-                    midpoint(s, b);
+                    sbits = (g4 & 1) ? (sw & 0xFFFF0000u) : (sw << 16);
+                    bbits = (g4 & 1) ? (bwd & 0xFFFF0000u) : (bwd << 16);
+                }
+                sj = __uint_as_float(live ? sbits : 0u);
+                bj = __uint_as_float(live ? bbits : 0u);
+                midpoint(sj, bj);
+            };
+#pragma unroll
+            for (int j = 0; j < ND; j++) {
+                float4_t d[2];
+#pragma unroll
+                for (int sl = 0; sl < NS; sl++) {
+                    const int g4 = j * NS + sl;
+                    const int gx = min(4 * qx + g4, groups - 1);
+                    // this lane's A rows carry activations for group g4 only in slot sl
+                    const uint4 *xg = (NS == 1 || sa == sl) ? xrow + 8 * gx : zrow;
+                    const half8_t a0 = __builtin_bit_cast(half8_t, xg[0]);
+                    const half8_t a1 = __builtin_bit_cast(half8_t, xg[1]);
+#pragma unroll
+                    for (int t = 0; t < 2; t++) {
+                        const int row = 16 * t + n16;
+                        // words 2kb, 2kb+1 of the group: chunk 2g4 + kb/2, bytes 8(kb%2) ..
+                        const uint2 bw = reinterpret_cast<const uint2 *>(
+                            scratch)[(row * 8 + ((2 * g4 + (kb >> 1)) ^ (row & 7))) * 2 + (kb & 1)];
+                        const uint32_t wd[2] = {bw.x, bw.y};
+#pragma unroll
+                        for (int i = 0; i < 2; i++) {
+                            const uint32_t w8 = wd[i] >> 8;
+                            const uint4 bq = {wd[i] & 0x000F000Fu, wd[i] & 0x00F000F0u,
+                                              w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+                            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                i == 0 ? a0 : a1, __builtin_bit_cast(half8_t, bq),
+                                (i == 0 && sl == 0) ? float4_t{} : d[t], 0, 0, 0);
+                        }
+                    }
+                }
+                // fold: this lane's group's scale on its sums, its bias on the group sums of
+                // its activation rows
+                const int gx = min(4 * qx + j * NS + kbd, groups - 1);
+                const float4_t xa4 = xsg[gx * 4 + (kb % (RG / 4))];
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    float sj, bj;
+                    sb_of(t, j, sj, bj);
 #pragma unroll
                     for (int v = 0; v < 4; v++)
                         acc[4 * t + v] =
-                            __builtin_fmaf(s, d[v], __builtin_fmaf(b, xa4[v], acc[4 * t + v]));
+                            __builtin_fmaf(sj, d[t][v], __builtin_fmaf(bj, xa4[v], acc[4 * t + v]));
                 }
             }
         } else {
@@ -738,6 +786,16 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16) ? 4 : 1) voi
             }
         }
         if (last) {
+            // 16x16x32 with several group slots: add the slots' sums of each activation row
+            // (lanes kb, kb ^ (RG/4), ...: xor 16 then 32 for 4 slots, xor 32 for 2), after
+            // which lanes kb < RG/4 hold rows 4kb .. 4kb+3 as with one slot
+            if constexpr (MF16 && NS > 1) {
+#pragma unroll
+                for (int i = 0; i < NACC; i++) {
+                    if constexpr (NS == 4) acc[i] += __shfl_xor(acc[i], 16, 64);
+                    acc[i] += __shfl_xor(acc[i], 32, 64);
+                }
+            }
             // combine the parts in LDS: parts 1..KS-1 publish, part 0 adds them in order
             if constexpr (KS > 1) {
                 float *pbuf =
@@ -794,32 +852,45 @@ typedef void (*MfmaFn)(const uint4 *, const uint16_t *, const uint16_t *, const 
 
 static bool use_mf16(int ks, int nb, long tiles)
 {
-    return Q4MV_MFMA_MF16 && ks <= 2 && tiles >= Q4MV_MFMA_KS4_BELOW && (nb <= 4 || nb > 8);
+    return Q4MV_MFMA_MF16 && ks <= 2 && tiles >= Q4MV_MFMA_KS4_BELOW &&
+           (nb <= 4 || nb > 8 || Q4MV_MFMA_MF16_R8);
 }
 
-template <int WPB, int KS, bool NB16, bool MF16>
+template <int WPB, int KS, bool NB16, bool MF16, bool R8 = false>
 static MfmaFn pick_sb(int sbw)
 {
     if constexpr (KS == 2 && WPB == kMfmaWaves)
-        if (sbw == 32) return mfma_kernel<WPB, KS, NB16, 32, MF16>;
-    return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16, MF16>
-           : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8, MF16>
-                      : mfma_kernel<WPB, KS, NB16, 2, MF16>;
+        if (sbw == 32) return mfma_kernel<WPB, KS, NB16, 32, MF16, 4, R8>;
+    return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16, MF16, 4, R8>
+           : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8, MF16, 4, R8>
+                      : mfma_kernel<WPB, KS, NB16, 2, MF16, 4, R8>;
 }
 
 // Low-bit codes: 8-wave blocks and 8- or 16-byte scale loads only (q4mv_lowbit checks).
 template <int BITS, int KS>
-static MfmaFn pick_lowbit_ks(bool nb16, int sbw, bool mf16)
+static MfmaFn pick_lowbit_ks(bool nb16, int sbw, bool mf16, bool r8)
 {
-    if constexpr (KS == 2)
-        if (sbw == 32)
-            return mf16   ? mfma_kernel<kMfmaWaves, KS, false, 32, true, BITS>
-                   : nb16 ? mfma_kernel<kMfmaWaves, KS, true, 32, false, BITS>
-                          : mfma_kernel<kMfmaWaves, KS, false, 32, false, BITS>;
     if constexpr (KS <= 2)
-        if (mf16)
+        if (mf16) {
+            // 16x16x32: the group slots follow nb (4 rows, 8 rows, or one slot of 16)
+            if constexpr (KS == 2)
+                if (sbw == 32)
+                    return nb16 ? mfma_kernel<kMfmaWaves, KS, true, 32, true, BITS>
+                           : r8 ? mfma_kernel<kMfmaWaves, KS, false, 32, true, BITS, true>
+                                : mfma_kernel<kMfmaWaves, KS, false, 32, true, BITS>;
+            if (nb16)
+                return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, true, 16, true, BITS>
+                                 : mfma_kernel<kMfmaWaves, KS, true, 8, true, BITS>;
+            if (r8)
+                return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, false, 16, true, BITS, true>
+                                 : mfma_kernel<kMfmaWaves, KS, false, 8, true, BITS, true>;
             return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, false, 16, true, BITS>
                              : mfma_kernel<kMfmaWaves, KS, false, 8, true, BITS>;
+        }
+    if constexpr (KS == 2)
+        if (sbw == 32)
+            return nb16 ? mfma_kernel<kMfmaWaves, KS, true, 32, false, BITS>
+                        : mfma_kernel<kMfmaWaves, KS, false, 32, false, BITS>;
     if (nb16)
         return sbw == 16 ? mfma_kernel<kMfmaWaves, KS, true, 16, false, BITS>
                          : mfma_kernel<kMfmaWaves, KS, true, 8, false, BITS>;
@@ -828,23 +899,25 @@ static MfmaFn pick_lowbit_ks(bool nb16, int sbw, bool mf16)
 }
 
 template <int BITS>
-static MfmaFn pick_lowbit(int ks, bool nb16, int sbw, bool mf16)
+static MfmaFn pick_lowbit(int ks, bool nb16, int sbw, bool mf16, bool r8)
 {
-    return ks == 1   ? pick_lowbit_ks<BITS, 1>(nb16, sbw, mf16)
-           : ks == 2 ? pick_lowbit_ks<BITS, 2>(nb16, sbw, mf16)
-           : ks == 4 ? pick_lowbit_ks<BITS, 4>(nb16, sbw, mf16)
-                     : pick_lowbit_ks<BITS, 8>(nb16, sbw, mf16);
+    return ks == 1   ? pick_lowbit_ks<BITS, 1>(nb16, sbw, mf16, r8)
+           : ks == 2 ? pick_lowbit_ks<BITS, 2>(nb16, sbw, mf16, r8)
+           : ks == 4 ? pick_lowbit_ks<BITS, 4>(nb16, sbw, mf16, r8)
+                     : pick_lowbit_ks<BITS, 8>(nb16, sbw, mf16, r8);
 }
 
 template <int WPB, int KS>
-static MfmaFn pick(bool nb16, int sbw, bool mf16)
+static MfmaFn pick(bool nb16, int sbw, bool mf16, bool r8)
 {
     // the 16x16x32 path covers 16 activation rows either way; nb > 8 gets an instance of its
     // own so that the register cap for two blocks per CU (tile-block scales, nb <= 8) does
     // not apply where the LDS allows only one
     if constexpr (KS <= 2)
         if (mf16)
-            return nb16 ? pick_sb<WPB, KS, true, true>(sbw) : pick_sb<WPB, KS, false, true>(sbw);
+            return nb16 ? pick_sb<WPB, KS, true, true>(sbw)
+                   : r8 ? pick_sb<WPB, KS, false, true, true>(sbw)
+                        : pick_sb<WPB, KS, false, true>(sbw);
     return nb16 ? pick_sb<WPB, KS, true, false>(sbw) : pick_sb<WPB, KS, false, false>(sbw);
 }
 
@@ -911,6 +984,7 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
     const MfmaShape sh = mfma_shape(klen, a.nb, tiles);
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
     const bool mf16 = use_mf16(sh.ks, a.nb, tiles);
+    const bool r8 = mf16 && a.nb > 4 && a.nb <= 8;  // 16x16x32 with two 8-row group slots
     const size_t lds0 = mfma_lds_bytes(klen, a.nb) + part_bytes(sh.wpb, sh.ks, a.nb, tiles);
     // 16-byte scale loads when the layout allows and their larger scratch still fits (every
     // row's slice of scales must start on an 8- or 16-byte boundary)
@@ -934,16 +1008,17 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
     MfmaFn fn;
     if (a.bits != 4) {
         if (sh.wpb != kMfmaWaves || sbw == 2) return hipErrorInvalidValue;  // checked on the host
-        fn = a.bits == 2 ? pick_lowbit<2>(sh.ks, nb16, sbw, mf16)
-                         : pick_lowbit<3>(sh.ks, nb16, sbw, mf16);
+        fn = a.bits == 2 ? pick_lowbit<2>(sh.ks, nb16, sbw, mf16, r8)
+                         : pick_lowbit<3>(sh.ks, nb16, sbw, mf16, r8);
     } else if (sh.wpb == kMfmaWaves)
-        fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sbw, mf16)
-             : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sbw, mf16)
-             : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sbw, mf16)
-                          : pick<kMfmaWaves, 8>(nb16, sbw, mf16);
+        fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sbw, mf16, r8)
+             : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sbw, mf16, r8)
+             : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sbw, mf16, r8)
+                          : pick<kMfmaWaves, 8>(nb16, sbw, mf16, r8);
     else
-        fn = sh.ks == 1 ? pick<4, 1>(nb16, sbw, mf16) : sh.ks == 2 ? pick<4, 2>(nb16, sbw, mf16)
-                                                              : pick<4, 4>(nb16, sbw, mf16);
+        fn = sh.ks == 1   ? pick<4, 1>(nb16, sbw, mf16, r8)
+             : sh.ks == 2 ? pick<4, 2>(nb16, sbw, mf16, r8)
+                          : pick<4, 4>(nb16, sbw, mf16, r8);
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
     const int tpb = sh.wpb / sh.ks;

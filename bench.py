@@ -607,6 +607,49 @@ def summarize_pmc(fetch_dir, write_dir, workload, nb, cmd, out_txt):
     print("\n".join(lines))
 
 
+def summarize_counters(dirs, workload, nb, cmd, out_txt):
+    """SQ counters of the GEMV kernel from rocprofv3 --pmc runs of `bench.py --pmc-probe`
+    (one directory per pass; each counter's median over the kernel's dispatches), with the
+    per-wave and per-cycle ratios they give."""
+    vals, kname, launches = {}, None, 0
+    for d in dirs:
+        for r in _read_csv_rows(d, "counter_collection.csv"):
+            k = r["Kernel_Name"]
+            if "valu_kernel" not in k and "mfma_kernel" not in k:
+                continue
+            kname = k
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no GEMV kernel counters under {dirs}")
+    med = {c: statistics.median(v) for c, v in vals.items()}
+    launches = max(len(v) for v in vals.values())
+    lines = [f"# SQ counters of {kname.split('(')[0]} on {workload} NB={nb}",
+             f"# command (one run per pass, COUNTERS = the pass's list): {cmd}",
+             f"# median over {launches} launches per counter (summed over the device)"]
+    lines += [f"{c} {med[c]:.0f}" for c in sorted(med)]
+    w = med.get("SQ_WAVES")
+    if w:
+        lines.append("# per wave:")
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD",
+                  "SQ_INSTS_SALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_ANY"):
+            if c in med:
+                lines.append(f"{c} / SQ_WAVES = {med[c] / w:.1f}")
+    wc = med.get("SQ_WAVE_CYCLES")
+    if wc:
+        lines.append("# share of the waves' lifetime:")
+        for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM"):
+            if c in med:
+                lines.append(f"{c} / SQ_WAVE_CYCLES = {med[c] / wc:.3f}")
+    bc = med.get("SQ_BUSY_CYCLES")
+    if bc and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+        lines.append(f"SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES = "
+                     f"{med['SQ_VALU_MFMA_BUSY_CYCLES'] / bc:.3f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def pmc_probe(workload, nb):
     import torch
     src = torch.full((CALIB_BYTES // 4,), 1.0, dtype=torch.float32, device="cuda")
@@ -638,6 +681,7 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR")
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="")
     ap.add_argument("--bench-log", help="bench.py output of the profiled run")
@@ -646,6 +690,9 @@ def main():
         return summarize_trace(args.summarize_trace, args.out, args.cmd, args.bench_log)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.workload, args.nb, args.cmd, args.out)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.workload, args.nb, args.cmd,
+                                  args.out)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the GEMV shards by output rows "
               "with no cross-GPU step in the kernel); run it with --gpus 1", file=sys.stderr)
