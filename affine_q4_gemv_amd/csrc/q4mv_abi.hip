@@ -9,17 +9,23 @@
 namespace q4mv_impl {
 
 // The automatic choice between the VALU dot-product kernels and the MFMA kernel, by the
-// activation rows and the 32-row tiles of one matrix. The MFMA kernel costs more per launch
-// (it stages every activation row in LDS, and each of its units runs on a 32-row tile
-// whatever nb is), the VALU kernels more per activation row. Measured crossovers on MI355X
-// (graph-timed fused launches, us, one-row VALU against MFMA):
+// activation rows and the 32-row tiles of one matrix (never by the number of matrices, so a
+// matrix gives the same bits alone, batched or as an expert slot). The MFMA kernel costs
+// more per launch (it stages every activation row in LDS, and each of its units runs on a
+// 32-row tile whatever nb is), the VALU kernels more per activation row and weight.
+// Measured on MI355X (graph-timed fused launches, us, one-row VALU against MFMA):
 //   2560 x 2560 (80 tiles)        nb 2: 5.2 / 7.0, nb 3: 6.0 / 7.2, nb 4: 6.9 / 7.6, nb 5: 9.9 / 7.9
 //   8 x 2560 x 640 (80 tiles)     nb 2: 6.1 / 7.3, nb 3: 6.7 / 7.4, nb 4: 7.5 / 7.6, nb 5: 8.7 / 7.6
+//   8 x 1280 x 2560 (40 tiles)    nb 4: the expert gate|up projection, about 3 us slower on
+//                                 the VALU kernel (the MoE MLP chain 21.7 against 18.6)
 //   9728 x 2560 (304 tiles)       nb 2: 7.7 / 8.7, nb 3: 9.1 / 8.9, nb 4: 10.6 / 9.3
 //   151936 x 2560 (4748 tiles)    nb 2: 46.2 / 40.5, nb 3: 56.6 / 41.4
-// so: the MFMA kernel from nb 5; at nb 3 and 4 from 256 tiles; at nb 2 from 1024 tiles.
-constexpr int kValuAutoMaxNB = 4;
-constexpr long kMfmaMinTilesNb34 = 256;
+// A single small matrix favours the VALU kernel up to nb 4, a batch of experts the MFMA
+// kernel from nb 4; a per-matrix rule cannot tell them apart, and the expert batches are the
+// case the batched kernels exist for. So: the MFMA kernel from nb 4; at nb 3 from 256 tiles;
+// at nb 2 from 1024 tiles.
+constexpr int kValuAutoMaxNB = 3;
+constexpr long kMfmaMinTilesNb3 = 256;
 constexpr long kMfmaMinTilesNb2 = 1024;
 
 // The automatic choice, from (nb, out_dim) only (the MFMA kernel runs K-sliced where the
@@ -32,7 +38,7 @@ int auto_path(int in_dim, int nb, bool two_row, int out_dim)
 {
     (void)in_dim;
     const long tiles = (out_dim + 31) / 32;
-    if (nb > kValuAutoMaxNB || (nb > 2 && tiles >= kMfmaMinTilesNb34) ||
+    if (nb > kValuAutoMaxNB || (nb == 3 && tiles >= kMfmaMinTilesNb3) ||
         (nb == 2 && tiles >= kMfmaMinTilesNb2))
         return kMfma;
     return two_row ? kValu2 : kValu1;

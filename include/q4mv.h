@@ -302,7 +302,7 @@ int q4mv_combine(const float *y, const float *wmap, float *out, int n_u, int nb,
 
 /* Which path (1, 2 or 3) the automatic dispatch of q4mv (two_row = 0) or q4mv_2row
    (two_row = 1) takes for this shape; a negative status if the shape is invalid. The MFMA
-   kernel for nb >= 5, for nb = 3, 4 on matrices of at least 256 32-row tiles
+   kernel for nb >= 4, for nb = 3 on matrices of at least 256 32-row tiles
    (out_dim > 8160) and for nb = 2 on matrices of at least 1024 tiles (out_dim > 32736);
    otherwise q4mv takes the one-row VALU kernel and q4mv_2row the two-row one (the two VALU
    kernels give bitwise the same result). in_dim does not enter the choice: every path takes

@@ -105,19 +105,18 @@ def test_auto_path(L):
     assert L.q4mv_auto_path(2560, 2, 0, 9) == 1       # short launches: one-row kernel
     assert L.q4mv_auto_path(2560, 2, 0, 10) == 1
     assert L.q4mv_auto_path(2560, 2, 0, 9728) == 1    # 304 tiles: one-row kernel at nb 2
-    assert L.q4mv_auto_path(2560, 3, 0, 9728) == 3    # and the MFMA kernel at nb 3 and 4
-    assert L.q4mv_auto_path(2560, 4, 0, 8192) == 3    # 256 tiles
-    assert L.q4mv_auto_path(2560, 4, 0, 8160) == 1    # 255 tiles
-    assert L.q4mv_auto_path(2560, 3, 0, 8160) == 1
-    assert L.q4mv_auto_path(2560, 5, 0, 32) == 3      # from nb 5 on every shape
+    assert L.q4mv_auto_path(2560, 3, 0, 9728) == 3    # and the MFMA kernel at nb 3
+    assert L.q4mv_auto_path(2560, 3, 0, 8192) == 3    # 256 tiles
+    assert L.q4mv_auto_path(2560, 3, 0, 8160) == 1    # 255 tiles
+    assert L.q4mv_auto_path(2560, 4, 0, 32) == 3      # from nb 4 on every shape
     assert L.q4mv_auto_path(640, 1, 1, 2560) == 2     # q4mv_2row: two-row kernel
     assert L.q4mv_auto_path(2560, 3, 1, 2560) == 2
     assert L.q4mv_auto_path(2560, 2, 0, 32768) == 3   # 1024 tiles: the MFMA kernel from 2 rows
     assert L.q4mv_auto_path(2560, 2, 1, 32768) == 3   # q4mv_2row follows q4mv onto it
     assert L.q4mv_auto_path(2560, 2, 0, 32737) == 3
     assert L.q4mv_auto_path(2560, 2, 0, 32736) == 1   # 1023 tiles
-    assert L.q4mv_auto_path(2560, 4, 0, 2560) == 1    # 80 tiles at nb 4: one-row kernel
-    assert L.q4mv_auto_path(640, 4, 1, 2560) == 2
+    assert L.q4mv_auto_path(2560, 4, 0, 2560) == 3
+    assert L.q4mv_auto_path(640, 4, 1, 2560) == 3
     assert L.q4mv_auto_path(2560, 16, 1, 2560) == 3
     assert L.q4mv_auto_path(8192, 16, 0, 8) == 3      # K-sliced where the row does not fit
     assert L.q4mv_auto_path(1 << 20, 16, 0, 8) == 3
