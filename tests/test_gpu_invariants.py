@@ -52,12 +52,21 @@ def test_batch_rows_bitwise(shape):
             assert torch.equal(yb[:, r, :], y1[:, 0, :]), (path, r)
 
 
+# (n_mat, out_dim, in_dim, nb): batches whose total tile count crosses the MFMA kernel's
+# launch-shape thresholds (256 and 1024 32-row tiles) while one matrix stays below them, so
+# a shape choice taken from the batch instead of the matrix would change the bits
+BATCHES = [(3, 130, 640, 4), (8, 2560, 2560, 4), (4, 8192, 2560, 4), (5, 6400, 1024, 12)]
+
+
 @pytest.mark.parametrize("path", [q4.PATH_VALU, q4.PATH_VALU_2ROW, q4.PATH_MFMA])
-def test_matrix_batch_bitwise(path):
-    case = workloads.make_shape(3, 130, 640, 4, seed=5)
+@pytest.mark.parametrize("n_mat,out_dim,in_dim,nb", BATCHES,
+                         ids=[f"{m}x{o}x{i}-nb{b}" for m, o, i, b in BATCHES])
+def test_matrix_batch_bitwise(path, n_mat, out_dim, in_dim, nb):
+    case = workloads.make_shape(n_mat, out_dim, in_dim, nb, seed=5 + out_dim)
     d = upload(case)
+    flush(f"[batch bitwise] {n_mat}x{out_dim}x{in_dim} nb={nb} path={path}")
     yb = run(d, path)
-    for m in range(3):
+    for m in range(n_mat):
         c1 = dict(case, codes=case["codes"][m:m + 1], scales=case["scales"][m:m + 1],
                   biases=case["biases"][m:m + 1], x=case["x"][m:m + 1])
         assert torch.equal(yb[m:m + 1], run(upload(c1), path)), m
