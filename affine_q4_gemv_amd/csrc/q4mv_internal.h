@@ -70,8 +70,8 @@ constexpr size_t kMaxLds = 160 * 1024;
 // per-wave staging votes and a zero operand (the partial-sum buffers of mfma_part_bytes come on top).
 inline size_t mfma_lds_bytes(int in_dim, int nb)
 {
-    // nb rows of 4C + 1 pair units, then groups x 16 sums, then 8 ints and 32 zero bytes
-    return (size_t)nb * (4 * (in_dim / 32) + 1) * 16 + (size_t)(in_dim / 64) * 16 * 4 + 64;
+    // nb rows of 4C + 1 pair units, then groups x 16 sums, then 16 ints and 32 zero bytes
+    return (size_t)nb * (4 * (in_dim / 32) + 1) * 16 + (size_t)(in_dim / 64) * 16 * 4 + 96;
 }
 // Partial-sum buffers of the MFMA kernel: 2 steps x tile groups per block x (ks - 1) parts
 // x lanes holding live rows x nacc accumulators.
@@ -80,9 +80,10 @@ inline size_t mfma_part_bytes(int wpb, int ks, int nacc, int lanes)
     return (size_t)2 * (wpb / ks) * (ks - 1) * lanes * nacc * 4;
 }
 // Launch shape of the MFMA kernel: waves per block and waves per tile (K-split); {0, 0} if
-// the shape's LDS does not fit in one compute unit.
+// the shape's LDS does not fit in one compute unit. need8: low-bit codes, which run on
+// 8-wave blocks with a K-split of 1, 2, 4 or 8.
 struct MfmaShape { int wpb, ks; };
-MfmaShape mfma_shape(int in_dim, int nb, long tiles);
+MfmaShape mfma_shape(int in_dim, int nb, long tiles, bool need8);
 // Columns per K slice of the MFMA kernel for a row of in_dim: in_dim when the staged
 // activations of the whole row fit in LDS, else the length of the fewest equal slices that
 // fit (8-wave blocks when need8); 0 if none does.

@@ -80,6 +80,11 @@
 #ifndef Q4MV_MFMA_MF16_R8
 #define Q4MV_MFMA_MF16_R8 1
 #endif
+// Short launches (fewer than KS8_BELOW tiles, nb <= 8) whose rows hold 3, 5, 6, 10 or 12
+// quads: one quad per wave (K-split = quads).
+#ifndef Q4MV_MFMA_KSQ
+#define Q4MV_MFMA_KSQ 1
+#endif
 // Tile-block scale loads (SBW = 32) where they apply.
 #ifndef Q4MV_MFMA_TBS
 #define Q4MV_MFMA_TBS 1
@@ -90,7 +95,8 @@
 
 namespace q4mv_impl {
 
-// Waves per block: 8 (two per SIMD), or 4 when the LDS of 8 does not fit.
+// Waves per block: 8 (two per SIMD), or 4 when the LDS of 8 does not fit; on short launches
+// with one quad per wave, the row's quad count (times two tile groups up to 6 quads).
 constexpr int kMfmaWaves = 8;
 // Per-wave LDS scratch of one unit: codes 32 rows x 128 B, then scales and biases
 // 2 x 32 rows x 8 B, or x 16 B with 16-byte scale loads (in 16-byte units).
@@ -180,10 +186,12 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     // the lanes that hold activation rows below nb).
     const int RS = 4 * C + 1;
     float4_t *const xsg_w = reinterpret_cast<float4_t *>(lds + nb * RS);
-    // one int per wave for the staging scale vote (32 bytes), two zero units (32 bytes: the
-    // A operand of rows outside their group slot), then the partial sums
+    // one int per wave for the staging scale vote (16 slots, 64 bytes), two zero units (32
+    // bytes: the A operand of rows outside their group slot), then the partial sums
+    static_assert(WPB <= 16, "one vote slot per wave");
     int *const vote = reinterpret_cast<int *>(xsg_w + groups * 4);
-    float *const part = reinterpret_cast<float *>(vote + 16);
+    int *const zero_units = vote + 16;
+    float *const part = reinterpret_cast<float *>(vote + 24);
     // lanes whose accumulators hold activation rows below nb (16x16x32: rows 4kb .. 4kb+3)
     const int plan = MF16 ? 16 * ((nb + 3) >> 2) : 64;
     uint4 *const scratch_all =
@@ -414,7 +422,7 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     // Each wave writes its own vote (so nothing needs clearing first); after the barrier
     // every thread reads all of them.
     auto stage = [&]() __attribute__((always_inline)) {
-        if (threadIdx.x < 8) vote[8 + threadIdx.x] = 0;  // the zero units
+        if (threadIdx.x < 8) zero_units[threadIdx.x] = 0;
         const int mine = __any(xf ? fstage(true) : pstage(true)) ? 1 : 0;
         if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = mine;
         __syncthreads();
@@ -596,7 +604,7 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     const uint4 *const xrow = MF16 ? lds + min(n16 % RG, nb - 1) * RS + 2 * kb
                                    : lds + min(n, nb - 1) * RS + 4 * h;
     // zeros for A rows outside their group's slot
-    const uint4 *const zrow = reinterpret_cast<const uint4 *>(vote + 8);
+    const uint4 *const zrow = reinterpret_cast<const uint4 *>(zero_units);
     float acc[NACC];
     // Low-bit codes reconstruct at the middle of the 4-bit range each stands for:
     // w = (4q + 1.5) s + b (Q2), (2q + 0.5) s + b (Q3); the fold takes K s and M s + b (formed
@@ -936,9 +944,35 @@ static int mfma_ks(long tiles, int quads)
     return ks;
 }
 
-MfmaShape mfma_shape(int in_dim, int nb, long tiles)
+// One quad per wave on short launches: the K-split equals the row's quads, for these quad
+// counts (rows of 640/768, 1280, 1536, 2560 and 3072 columns), with two tile groups per
+// block where the K-split is at most 6. Measured (fused launches, us, against K-split 8 or 2
+// with up to two units per wave): 2560 x 2560 NB 4 7.56 -> 6.41, NB 8 8.48 -> 7.56;
+// 8 x 2560 x 640 NB 4 7.56 -> 6.88, NB 8 7.70 -> 7.13. From 256 tiles on the grid outgrows
+// one round (9728 x 2560 NB 4 9.31 -> 9.76 with a K-split of 10), and above nb 8 the staging
+// of 16 rows per block outweighs it (8 x 2560 x 640 NB 16 8.58 -> 10.89).
+static int ksq_waves(int quads)
+{
+    switch (quads) {
+    case 3: return 6;
+    case 5: return 10;
+    case 6: return 12;
+    case 10: return 10;
+    case 12: return 12;
+    default: return 0;
+    }
+}
+
+MfmaShape mfma_shape(int in_dim, int nb, long tiles, bool need8)
 {
     const int quads = (in_dim / 64 + 3) / 4;
+    if (Q4MV_MFMA_KSQ && !need8 && nb <= 8 && tiles < Q4MV_MFMA_KS8_BELOW &&
+        ksq_waves(quads) != 0) {
+        const int wpb = ksq_waves(quads);
+        if (mfma_lds_bytes(in_dim, nb) + (size_t)wpb * kScratchUnits * 16 +
+                part_bytes(wpb, quads, nb, tiles) <= kMaxLds)
+            return {wpb, quads};
+    }
     // 8 waves per block when the activations, the per-wave scratch and the partial sums fit
     // in LDS (with a smaller K-split if need be), else 4 waves
     for (int wpb = kMfmaWaves; wpb >= 4; wpb >>= 1) {
@@ -959,7 +993,7 @@ static int mfma_slice_align(int in_dim)
 int mfma_slice(int in_dim, int nb, long tiles, bool need8)
 {
     auto ok = [&](int len) {
-        const MfmaShape sh = mfma_shape(len, nb, tiles);
+        const MfmaShape sh = mfma_shape(len, nb, tiles, need8);
         return sh.wpb != 0 && (!need8 || sh.wpb == kMfmaWaves);
     };
     if (ok(in_dim)) return in_dim;
@@ -981,7 +1015,7 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
     const long tiles = (a.out_dim + 31) / 32;
     // every choice that changes the arithmetic (K-split, matrix-core shape) comes from one
     // matrix's tile count, so a matrix gives the same bits alone, batched or as an expert slot
-    const MfmaShape sh = mfma_shape(klen, a.nb, tiles);
+    const MfmaShape sh = mfma_shape(klen, a.nb, tiles, a.bits != 4);
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
     const bool mf16 = use_mf16(sh.ks, a.nb, tiles);
     const bool r8 = mf16 && a.nb > 4 && a.nb <= 8;  // 16x16x32 with two 8-row group slots
@@ -1005,20 +1039,35 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
         sbw = 32;
     const size_t lds =
         lds0 + (size_t)sh.wpb * scratch_units(sbw) * 16 + (sbw == 32 ? tb_bytes : 0);
-    MfmaFn fn;
+    // the instance of exactly this (waves, K-split); any other pair is an error, never a
+    // kernel of another shape
+    MfmaFn fn = nullptr;
+    const int wk = sh.wpb * 100 + sh.ks;
     if (a.bits != 4) {
         if (sh.wpb != kMfmaWaves || sbw == 2) return hipErrorInvalidValue;  // checked on the host
-        fn = a.bits == 2 ? pick_lowbit<2>(sh.ks, nb16, sbw, mf16, r8)
-                         : pick_lowbit<3>(sh.ks, nb16, sbw, mf16, r8);
-    } else if (sh.wpb == kMfmaWaves)
-        fn = sh.ks == 1   ? pick<kMfmaWaves, 1>(nb16, sbw, mf16, r8)
-             : sh.ks == 2 ? pick<kMfmaWaves, 2>(nb16, sbw, mf16, r8)
-             : sh.ks == 4 ? pick<kMfmaWaves, 4>(nb16, sbw, mf16, r8)
-                          : pick<kMfmaWaves, 8>(nb16, sbw, mf16, r8);
-    else
-        fn = sh.ks == 1   ? pick<4, 1>(nb16, sbw, mf16, r8)
-             : sh.ks == 2 ? pick<4, 2>(nb16, sbw, mf16, r8)
-                          : pick<4, 4>(nb16, sbw, mf16, r8);
+        if (sh.ks == 1 || sh.ks == 2 || sh.ks == 4 || sh.ks == 8)
+            fn = a.bits == 2 ? pick_lowbit<2>(sh.ks, nb16, sbw, mf16, r8)
+                             : pick_lowbit<3>(sh.ks, nb16, sbw, mf16, r8);
+    } else {
+        switch (wk) {
+        case 801: fn = pick<8, 1>(nb16, sbw, mf16, r8); break;
+        case 802: fn = pick<8, 2>(nb16, sbw, mf16, r8); break;
+        case 804: fn = pick<8, 4>(nb16, sbw, mf16, r8); break;
+        case 808: fn = pick<8, 8>(nb16, sbw, mf16, r8); break;
+        case 401: fn = pick<4, 1>(nb16, sbw, mf16, r8); break;
+        case 402: fn = pick<4, 2>(nb16, sbw, mf16, r8); break;
+        case 404: fn = pick<4, 4>(nb16, sbw, mf16, r8); break;
+#if Q4MV_MFMA_KSQ
+        case 603: fn = pick<6, 3>(nb16, sbw, mf16, r8); break;
+        case 1005: fn = pick<10, 5>(nb16, sbw, mf16, r8); break;
+        case 1206: fn = pick<12, 6>(nb16, sbw, mf16, r8); break;
+        case 1010: fn = pick<10, 10>(nb16, sbw, mf16, r8); break;
+        case 1212: fn = pick<12, 12>(nb16, sbw, mf16, r8); break;
+#endif
+        default: break;
+        }
+    }
+    if (!fn) return hipErrorInvalidValue;
     hipError_t e = ensure_lds(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
     const int tpb = sh.wpb / sh.ks;

@@ -90,7 +90,11 @@ def test_lm_head_sampled(oracle_lib, nb):
 RAGGED = [(1, 1, 64, 1), (2, 3, 128, 2), (3, 5, 192, 3), (1, 257, 320, 1), (2, 130, 576, 5),
           (1, 1000, 4096, 2), (1, 77, 8192, 1), (1, 64, 16384, 4), (2, 33, 640, 16),
           (1, 2, 1024, 16), (1, 31, 4096, 16), (3, 18, 448, 7), (1, 4098, 2560, 9),
-          (1, 10, 7168, 3)]
+          (1, 10, 7168, 3),
+          # short launches with one quad per wave (rows of 3, 5, 6, 10, 12 quads; the last
+          # quad partly filled at 704 and 1216 columns)
+          (2, 100, 768, 4), (1, 77, 1280, 8), (1, 45, 1536, 7), (1, 300, 3072, 8),
+          (3, 70, 704, 6), (1, 33, 1216, 5), (1, 2600, 2560, 4), (4, 64, 640, 16)]
 
 
 @pytest.mark.parametrize("shape", RAGGED, ids=["x".join(map(str, s)) for s in RAGGED])
