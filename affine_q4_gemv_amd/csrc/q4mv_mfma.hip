@@ -603,6 +603,13 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     const int sa = n16 / RG, kbd = kb / (RG / 4);
     const uint4 *const xrow = MF16 ? lds + min(n16 % RG, nb - 1) * RS + 2 * kb
                                    : lds + min(n, nb - 1) * RS + 4 * h;
+    // 16x16x32: this lane's scratch word offset (8-byte words) of group g4 of a unit, for
+    // row n16 (row 16 + n16 is 256 words further on: the XOR swizzle of rows n16 and
+    // 16 + n16 is the same)
+    int boff[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; g4++)
+        boff[g4] = (n16 * 8 + ((2 * g4 + (kb >> 1)) ^ (n16 & 7))) * 2 + (kb & 1);
     // zeros for A rows outside their group's slot
     const uint4 *const zrow = reinterpret_cast<const uint4 *>(zero_units);
     float acc[NACC];
@@ -689,11 +696,13 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
             auto sb_of = [&](int t, int j, float &sj, float &bj) __attribute__((always_inline)) {
                 const int g4 = j * NS + kbd;
                 const int g = 4 * qx + g4;
-                const bool live = qd < q_end && g < groups;
+                // with tile-block scales every group of every unit is live (whole rows of 8k
+                // groups split in two equal parts of whole quads), so no mask and no clamp
+                const bool live = SBW == 32 || (qd < q_end && g < groups);
                 uint32_t sbits, bbits;
                 if constexpr (SBW == 32 && NS > 1) {
                     const int row = 16 * t + n16;
-                    const int gx = min(g, groups - 1);
+                    const int gx = SBW == 32 ? g : min(g, groups - 1);
                     sbits = (uint32_t)tbs[row * groups + gx] << 16;
                     bbits = (uint32_t)tbs[(32 + row) * groups + gx] << 16;
                 } else {
@@ -712,17 +721,16 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
 #pragma unroll
                 for (int sl = 0; sl < NS; sl++) {
                     const int g4 = j * NS + sl;
-                    const int gx = min(4 * qx + g4, groups - 1);
+                    const int gx = SBW == 32 ? 4 * qx + g4 : min(4 * qx + g4, groups - 1);
                     // this lane's A rows carry activations for group g4 only in slot sl
                     const uint4 *xg = (NS == 1 || sa == sl) ? xrow + 8 * gx : zrow;
                     const half8_t a0 = __builtin_bit_cast(half8_t, xg[0]);
                     const half8_t a1 = __builtin_bit_cast(half8_t, xg[1]);
 #pragma unroll
                     for (int t = 0; t < 2; t++) {
-                        const int row = 16 * t + n16;
                         // words 2kb, 2kb+1 of the group: chunk 2g4 + kb/2, bytes 8(kb%2) ..
-                        const uint2 bw = reinterpret_cast<const uint2 *>(
-                            scratch)[(row * 8 + ((2 * g4 + (kb >> 1)) ^ (row & 7))) * 2 + (kb & 1)];
+                        // of row 16t + n16 (the half's 16 rows are 2 KB further on)
+                        const uint2 bw = reinterpret_cast<const uint2 *>(scratch)[boff[g4] + 256 * t];
                         const uint32_t wd[2] = {bw.x, bw.y};
 #pragma unroll
                         for (int i = 0; i < 2; i++) {
@@ -737,7 +745,8 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
                 }
                 // fold: this lane's group's scale on its sums, its bias on the group sums of
                 // its activation rows
-                const int gx = min(4 * qx + j * NS + kbd, groups - 1);
+                const int gx = SBW == 32 ? 4 * qx + j * NS + kbd
+                                         : min(4 * qx + j * NS + kbd, groups - 1);
                 const float4_t xa4 = xsg[gx * 4 + (kb % (RG / 4))];
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
