@@ -36,6 +36,12 @@ constexpr int kValuMaxNB = 8;  // nb > 8 runs as two launches over activation-ro
 #ifndef Q4MV_VALU1_BLOCKS_PER_CU
 #define Q4MV_VALU1_BLOCKS_PER_CU 2  // one-row kernel
 #endif
+// ... and on long launches (every wave of a two-blocks-per-CU grid running at least
+// SBLDS_MIN_STEPS row steps): LM head NB=1 35.57 -> 34.90 us with 3 (35.00 with 4); short
+// launches are slower with more blocks (9728 x 2560 NB=1 5.90 -> 6.55 us with 3)
+#ifndef Q4MV_VALU1_BLOCKS_PER_CU_LONG
+#define Q4MV_VALU1_BLOCKS_PER_CU_LONG 3
+#endif
 #ifndef Q4MV_VALU_PREFETCH
 #define Q4MV_VALU_PREFETCH 0
 #endif
@@ -762,10 +768,11 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp,
     // block-loaded scales (one-row kernel, nb = 1, whole rows) when the waves of two blocks
     // per CU would each run several steps
     const bool prefetch = a.bits == 4 ? kValuPrefetch : Q4MV_LOWBIT_PREFETCH != 0;
+    const bool long_launch =
+        wave_steps * a.n_mat >= (long)Q4MV_VALU_SBLDS_MIN_STEPS * device_cus() * 2 * 4;
     const int nseg =
         prefetch || rows != 1 || nbp != 1 || klen != a.in_dim ||
-                !((Q4MV_VALU_SBLDS_BITS >> a.bits) & 1) ||
-                wave_steps * a.n_mat < (long)Q4MV_VALU_SBLDS_MIN_STEPS * device_cus() * 2 * 4
+                !((Q4MV_VALU_SBLDS_BITS >> a.bits) & 1) || !long_launch
             ? 0 : valu_sb_segs(rows, cpl, valu_specialised(log2g, cpl, a.bits));
     ValuFn fn = a.bits == 2   ? pick<2>(rows, nbp, log2g, cpl, nseg > 0)
                 : a.bits == 3 ? pick<3>(rows, nbp, log2g, cpl, nseg > 0)
@@ -778,8 +785,9 @@ static hipError_t launch_valu_part(const GemvArgs &a, int rows, int r0, int nbp,
     // (one round of blocks sized to the row steps, so that no wave runs a second step, was
     // measured slower on the 9728 x 2560 projection: 6.65 against 5.97 us)
     const long per_cu = std::min<long>(rows != 1      ? Q4MV_VALU_BLOCKS_PER_CU
-                                       : a.bits == 4 ? Q4MV_VALU1_BLOCKS_PER_CU
-                                                     : Q4MV_LOWBIT1_BLOCKS_PER_CU,
+                                       : a.bits != 4 ? Q4MV_LOWBIT1_BLOCKS_PER_CU
+                                       : long_launch ? Q4MV_VALU1_BLOCKS_PER_CU_LONG
+                                                     : Q4MV_VALU1_BLOCKS_PER_CU,
                                        resident_blocks(reinterpret_cast<const void *>(fn),
                                                        kValuThreads, lds));
     const long cap = std::max(1L, (long)device_cus() * per_cu / a.n_mat);
