@@ -85,6 +85,12 @@
 #ifndef Q4MV_MFMA_KSQ
 #define Q4MV_MFMA_KSQ 1
 #endif
+// nb 5..8 on many tiles: two 4-wave blocks per CU instead of one 8-wave block (the staged
+// rows of 8 activations leave room for one 8-wave block): LM head NB 6 44.2 -> 43.6 us,
+// NB 8 45.0 -> 44.8 us.
+#ifndef Q4MV_MFMA_NB8_WPB4
+#define Q4MV_MFMA_NB8_WPB4 1
+#endif
 // Tile-block scale loads (SBW = 32) where they apply.
 #ifndef Q4MV_MFMA_TBS
 #define Q4MV_MFMA_TBS 1
@@ -876,7 +882,7 @@ static bool use_mf16(int ks, int nb, long tiles)
 template <int WPB, int KS, bool NB16, bool MF16, bool R8 = false>
 static MfmaFn pick_sb(int sbw)
 {
-    if constexpr (KS == 2 && WPB == kMfmaWaves)
+    if constexpr (KS == 2 && (WPB == kMfmaWaves || (Q4MV_MFMA_NB8_WPB4 && WPB == 4)))
         if (sbw == 32) return mfma_kernel<WPB, KS, NB16, 32, MF16, 4, R8>;
     return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16, MF16, 4, R8>
            : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8, MF16, 4, R8>
@@ -982,6 +988,12 @@ MfmaShape mfma_shape(int in_dim, int nb, long tiles, bool need8)
                 part_bytes(wpb, quads, nb, tiles) <= kMaxLds)
             return {wpb, quads};
     }
+    // nb 5..8 on many tiles: 4-wave blocks where two of them (with tile-block scales) fit
+    if (Q4MV_MFMA_NB8_WPB4 && !need8 && nb > 4 && nb <= 8 && tiles >= Q4MV_MFMA_KS4_BELOW) {
+        const size_t base = mfma_lds_bytes(in_dim, nb) + (size_t)4 * kScratchUnits * 16;
+        if (base + part_bytes(4, 2, nb, tiles) + 2 * 128 * (size_t)(in_dim / 64) <= kMaxLds / 2)
+            return {4, 2};
+    }
     // 8 waves per block when the activations, the per-wave scratch and the partial sums fit
     // in LDS (with a smaller K-split if need be), else 4 waves
     for (int wpb = kMfmaWaves; wpb >= 4; wpb >>= 1) {
@@ -1041,7 +1053,8 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
     // tile-block scales (K-split 2, whole rows of 8k groups, full tiles) where their LDS
     // buffers fit next to the rest
     const size_t tb_bytes = (size_t)(sh.wpb / std::max(1, sh.ks)) * 128 * groups;
-    if (Q4MV_MFMA_TBS && sh.ks == 2 && sh.wpb == kMfmaWaves && groups % 8 == 0 &&
+    const bool tb_waves = sh.wpb == kMfmaWaves || (Q4MV_MFMA_NB8_WPB4 && sh.wpb == 4);
+    if (Q4MV_MFMA_TBS && sh.ks == 2 && tb_waves && groups % 8 == 0 &&
         groups <= kTbMaxGroups && klen == a.in_dim && a.out_dim >= 32 &&
         (uintptr_t)a.scales % 16 == 0 && (uintptr_t)a.biases % 16 == 0 &&
         lds0 + (size_t)sh.wpb * scratch_units(32) * 16 + tb_bytes <= kMaxLds)
