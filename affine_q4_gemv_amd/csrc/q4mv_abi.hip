@@ -116,8 +116,9 @@ static int check_weights(const uint32_t *w, const uint16_t *scales, const uint16
                          float *y, int n_mat, int out_dim, int in_dim, int nb)
 {
     if (!w || !scales || !biases || !y) return Q4MV_ERR_NULL;
-    if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
-        nb > Q4MV_MAX_NB)
+    // (matrices are the grid's second dimension, at most 65535 blocks)
+    if (n_mat < 1 || n_mat > 65535 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 ||
+        nb < 1 || nb > Q4MV_MAX_NB)
         return Q4MV_ERR_SHAPE;
     if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(biases, 2) || !aligned(y, 4))
         return Q4MV_ERR_ALIGN;
@@ -298,8 +299,8 @@ int q4mv_lowbit(int bits, const uint32_t *w, const uint16_t *scales, const uint1
 {
     if (!w || !scales || !biases || !xe || !xo || !xsum || !y) return Q4MV_ERR_NULL;
     if (bits != 2 && bits != 3) return Q4MV_ERR_VALUE;
-    if (n_mat < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 || nb < 1 ||
-        nb > Q4MV_MAX_NB)
+    if (n_mat < 1 || n_mat > 65535 || out_dim < 1 || in_dim < 64 || in_dim % 64 != 0 ||
+        nb < 1 || nb > Q4MV_MAX_NB)
         return Q4MV_ERR_SHAPE;
     if (!aligned(w, 8) || !aligned(xe, 16) || !aligned(xo, 16) || !aligned(scales, 2) ||
         !aligned(biases, 2) || !aligned(xsum, 4) || !aligned(y, 4))

@@ -116,7 +116,7 @@ int q4mv_prepare_x(const float *x, int n_rows, int in_dim, void *xe, void *xo, f
  * as K slices of the columns, one launch per slice in column order, each later slice adding
  * its partial product to what y holds (y is then read as well as written). The slices
  * depend on (in_dim, nb, out_dim) only.
- * Errors: NULL pointer; n_mat < 1, out_dim < 1, in_dim < 64, in_dim % 64 != 0,
+ * Errors: NULL pointer; n_mat outside 1..65535, out_dim < 1, in_dim < 64, in_dim % 64 != 0,
  * nb outside 1..Q4MV_MAX_NB (SHAPE); w, xe or xo not 16-byte aligned, scales/biases not
  * 2-byte, xsum/y not 4-byte aligned (ALIGN); launch failure.
  */

@@ -60,8 +60,8 @@ def test_gemv_validation(L, fn):
     f = getattr(L, fn)
     for k in ("w", "s", "b", "xe", "xo", "xsum", "y"):
         assert f(*gemv_args(**{k: None}), None) == ENULL
-    for kw in (dict(n_mat=0), dict(out=0), dict(ind=0), dict(ind=96), dict(ind=32),
-               dict(nb=0), dict(nb=17), dict(ind=-64)):
+    for kw in (dict(n_mat=0), dict(n_mat=65536), dict(out=0), dict(ind=0), dict(ind=96),
+               dict(ind=32), dict(nb=0), dict(nb=17), dict(ind=-64)):
         assert f(*gemv_args(**kw), None) == ESHAPE, kw
     for kw in (dict(w=A + 4), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1), dict(b=A + 1),
                dict(xsum=A + 2), dict(y=A + 1)):
@@ -209,8 +209,8 @@ def test_lowbit_validation(L):
     for bits in (2, 3):
         for k in ("w", "s", "b", "xe", "xo", "xsum", "y"):
             assert f(bits, *gemv_args(**{k: None}), 0, None) == ENULL, k
-        for kw in (dict(n_mat=0), dict(out=0), dict(ind=96), dict(ind=32), dict(nb=0),
-                   dict(nb=17)):
+        for kw in (dict(n_mat=0), dict(n_mat=65536), dict(out=0), dict(ind=96), dict(ind=32),
+                   dict(nb=0), dict(nb=17)):
             assert f(bits, *gemv_args(**kw), 0, None) == ESHAPE, kw
         for kw in (dict(w=A + 4), dict(xe=A + 8), dict(xo=A + 2), dict(s=A + 1), dict(xsum=A + 2),
                    dict(y=A + 1)):
