@@ -134,6 +134,25 @@ __device__ __forceinline__ XWord x_word(const float (&f)[8])
     return w;
 }
 
+// Q2/Q3 codes in the Q4 nibble layout. One 32-code chunk (upper words u0, u1; Q3's low-bit
+// word l) -> its four Q4 words: Q4 word 2i + j, nibble p is the code of column
+// 32c + 16i + 8j + p, whose 2-bit field (Q2, or Q3's upper two bits) sits at bit 4p + 2j of
+// upper word i and whose Q3 lowest bit at bit 4p + 2i + j of the low-bit word: a shift and a
+// mask per word (Q3: the upper field one bit up, the lowest bit merged below it). The codes
+// stay below 8, so every masked nibble field of the Q4 split is a subnormal f16 pattern.
+template <int BITS>
+__device__ __forceinline__ uint4 lowbit_chunk_to_q4(uint32_t u0, uint32_t u1, uint32_t l)
+{
+    if constexpr (BITS == 2)
+        return uint4{u0 & 0x33333333u, (u0 >> 2) & 0x33333333u, u1 & 0x33333333u,
+                     (u1 >> 2) & 0x33333333u};
+    else
+        return uint4{((u0 << 1) & 0x66666666u) | (l & 0x11111111u),
+                     ((u0 >> 1) & 0x66666666u) | ((l >> 1) & 0x11111111u),
+                     ((u1 << 1) & 0x66666666u) | ((l >> 2) & 0x11111111u),
+                     ((u1 >> 1) & 0x66666666u) | ((l >> 3) & 0x11111111u)};
+}
+
 // Whether a packed maximum of f16 magnitude patterns reaches 4096 (or is NaN / inf).
 __device__ __forceinline__ int mag_big(uint32_t m)
 {

@@ -118,32 +118,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // 2-byte values (compact loads).
 struct SbRegs { uint32_t v[4]; };
 
-// Q2/Q3 codes (the low-bit layouts of the VALU kernels) in the Q4 nibble layout, so the
-// rest of the kernel is unchanged: 2-bit fields at bits 2k and 16 + 2k of t (k < 4) move to
-// nibbles k and 4 + k.
-__device__ __forceinline__ uint32_t spread2(uint32_t t)
-{
-    t = (t | (t << 4)) & 0x0F0F0F0Fu;
-    return (t | (t << 2)) & 0x33333333u;
-}
-
-// One 32-code chunk, {upper word 0, upper word 1, low-bit word (Q3), 0} -> its four Q4 words:
-// Q4 word 2i + u, nibble p is the code of column 32c + 16i + 8u + p, whose 2-bit field (Q2,
-// or Q3's upper two bits) sits in word i at bit (p < 4 ? 0 : 16) + 2(4u + (p & 3)), and
-// whose Q3 lowest bit sits in the low-bit word at bit (p < 4 ? 0 : 16) + 8u + 2(p & 3) + i.
+// Low-bit chunks enter through lowbit_to_q4 (q4mv_device.h): the same Q4 nibble words as a
+// Q4 chunk, so the rest of the kernel is unchanged.
 template <int BITS>
 __device__ __forceinline__ u32x4 lowbit_to_q4(const u32x4 v)
 {
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-            uint32_t q = spread2((v[i] >> (8 * u)) & 0x00FF00FFu);
-            if constexpr (BITS == 3) q = (q << 1) | spread2((v[2] >> (8 * u + i)) & 0x00550055u);
-            o[2 * i + u] = q;
-        }
-    return o;
+    const uint4 o = lowbit_chunk_to_q4<BITS>(v[0], v[1], v[2]);
+    return u32x4{o.x, o.y, o.z, o.w};
 }
 
 // WPB: waves per block. KS: waves per tile (K-split). NB16: activation rows 8..15 are live

@@ -24,10 +24,10 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint2 *__restrict
 
 // Low-bit pack (the stores behind fn_q2_rows_h / fn_q3_rows_h on the Constant BATCH_MSL page):
 // one thread per (row, 32-code chunk). The code kept is the 4-bit code's top BITS bits;
-// column 16i + 8u + p of the chunk (u < 2, p < 8) goes to bit (p < 4 ? 0 : 16) + 2(4u + p%4)
-// of word i (Q2 word, or Q3 upper-two-bit word), and for Q3 its lowest bit to bit
-// (p < 4 ? 0 : 16) + 8u + 2(p%4) + i of the chunk's lowest-bit word. Rows are C*BITS words:
-// Q2 2 words per chunk; Q3 the 2C upper words, then the C lowest-bit words.
+// column 16i + 8u + p of the chunk (u < 2, p < 8) goes to bit 4p + 2u of word i (Q2 word, or
+// Q3 upper-two-bit word), and for Q3 its lowest bit to bit 4p + 2i + u of the chunk's
+// lowest-bit word. Rows are C*BITS words: Q2 2 words per chunk; Q3 the 2C upper words, then
+// the C lowest-bit words.
 template <int BITS>
 __global__ __launch_bounds__(256) void pack_lowbit_kernel(const uint4 *__restrict__ codes,
                                                           uint32_t *__restrict__ w,
@@ -49,12 +49,11 @@ __global__ __launch_bounds__(256) void pack_lowbit_kernel(const uint4 *__restric
         const uint32_t q4 = (b[col >> 2] >> (8 * (col & 3))) & 0xFu;
         const uint32_t q = q4 >> (4 - BITS);
         const int wi = col >> 4, u = (col >> 3) & 1, p = col & 7;
-        const int half = p < 4 ? 0 : 16;
         if constexpr (BITS == 2) {
-            word[wi] |= q << (half + 2 * (4 * u + (p & 3)));
+            word[wi] |= q << (4 * p + 2 * u);
         } else {
-            word[wi] |= (q >> 1) << (half + 2 * (4 * u + (p & 3)));
-            low |= (q & 1u) << (half + 8 * u + 2 * (p & 3) + wi);
+            word[wi] |= (q >> 1) << (4 * p + 2 * u);
+            low |= (q & 1u) << (4 * p + 2 * wi + u);
         }
     }
     uint32_t *wr = w + row * C * BITS;

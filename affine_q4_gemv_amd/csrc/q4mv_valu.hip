@@ -108,11 +108,12 @@ constexpr int valu_sb_segs(int rows, int cpl, bool specialised)
 // Constant BATCH_MSL page): the 4-bit code's top 2 or 3 bits, reconstructed at the middle of
 // the dropped range, w = (4q + 1.5) s + b and w = (2q + 0.5) s + b. A chunk of 32 codes is 2
 // words (Q2) or 2 + 1 words (Q3: upper-two-bit plane and lowest-bit plane); the layouts put
-// each code where a mask lands it in the f16 lane of the pair-layout activation it meets:
+// each code in the nibble of its column within its 8-column word, so that one shift and one
+// mask per word (lowbit_chunk_to_q4) give the Q4 nibble layout (Q2 is split in place):
 //   Q2 word i of chunk c covers columns 32c+16i .. +15; column 32c+16i+8u+p (u < 2, p < 8)
-//      is the 2-bit field at bit (p < 4 ? 0 : 16) + 2*(4u + (p & 3)).
+//      is the 2-bit field at bit 4p + 2u.
 //   Q3 upper words: the code's upper two bits at those positions; lowest-bit word of chunk c:
-//      the low bit of column 32c+16i+8u+p at bit (p < 4 ? 0 : 16) + 8u + 2*(p & 3) + i.
+//      the low bit of column 32c+16i+8u+p at bit 4p + 2i + u.
 // Row layout: Q4 C chunks of 4 words; Q2 C chunks of 2 words; Q3 the 2C upper words, then
 // the C lowest-bit words. So a row is C * BITS words in every case.
 
@@ -141,13 +142,30 @@ __device__ __forceinline__ uint4 load_chunk(const uint32_t *wr, int c, int C)
 }
 
 // Split one chunk into 16 f16 pairs: h[J][m] meets pair P_m of activation word J (pair
-// layout, x_unit). Q4: P0 and P2 come out as q*2^-24, P1 and P3 as 16q*2^-24. Q2 and Q3:
-// P_m comes out as 4^m q*2^-24.
+// layout, x_unit), masked fields read as f16 subnormals. Q4 (and Q3, first moved into the Q4
+// nibble layout): P0 and P2 come out as q*2^-24, P1 and P3 as 16q*2^-24. Q2 is split in
+// place, one shift per word: word i holds activation words 2i (fields at 4p) and 2i+1
+// (fields at 4p+2), so P0/P2 of J = 2i come out as q*2^-24, of J = 2i+1 as 4q*2^-24, and
+// P1/P3 as 16q and 64q (times 2^-24).
 template <int BITS>
 __device__ __forceinline__ void split_chunk(const uint4 cw, uint32_t (&h)[4][4])
 {
-    if constexpr (BITS == 4) {
-        const uint32_t wd[4] = {cw.x, cw.y, cw.z, cw.w};
+    if constexpr (BITS == 2) {
+        const uint32_t wd[2] = {cw.x, cw.y};
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const uint32_t w8 = wd[i] >> 8;
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                h[2 * i + u][0] = wd[i] & (0x00030003u << (2 * u));
+                h[2 * i + u][1] = wd[i] & (0x00300030u << (2 * u));
+                h[2 * i + u][2] = w8 & (0x00030003u << (2 * u));
+                h[2 * i + u][3] = w8 & (0x00300030u << (2 * u));
+            }
+        }
+    } else {
+        const uint4 q = BITS == 4 ? cw : lowbit_chunk_to_q4<BITS>(cw.x, cw.y, cw.z);
+        const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int J = 0; J < 4; J++) {
             const uint32_t w8 = wd[J] >> 8;
@@ -156,40 +174,31 @@ __device__ __forceinline__ void split_chunk(const uint4 cw, uint32_t (&h)[4][4])
             h[J][2] = w8 & 0x000F000Fu;
             h[J][3] = w8 & 0x00F000F0u;
         }
-    } else if constexpr (BITS == 2) {
-        const uint32_t wd[2] = {cw.x, cw.y};
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const uint32_t w8 = wd[i] >> 8;
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                h[2 * i][m] = wd[i] & (0x00030003u << (2 * m));
-                h[2 * i + 1][m] = w8 & (0x00030003u << (2 * m));
-            }
-        }
-    } else {
-        // code = 2 * upper + lowest: the upper field moved up one bit, the lowest bit below it
-        const uint32_t wd[2] = {cw.x, cw.y};
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const uint32_t ua = wd[i] << 1, ub = wd[i] >> 7;
-            const uint32_t la = cw.z >> i, lb = cw.z >> (8 + i);
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                h[2 * i][m] = (ua & (0x00060006u << (2 * m))) | (la & (0x00010001u << (2 * m)));
-                h[2 * i + 1][m] =
-                    (ub & (0x00060006u << (2 * m))) | (lb & (0x00010001u << (2 * m)));
-            }
-        }
     }
 }
 
 // sum(q * x) * 2^-24 of one chunk and one activation row from its split codes and the
-// row's four pair-layout units.
+// row's four pair-layout units: one accumulator per unit of the split.
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(const uint32_t (&h)[4][4], const uint4 (&xp)[4])
 {
-    if constexpr (BITS == 4) {
+    if constexpr (BITS == 2) {
+        // a[(J & 1) + 2 * (m & 1)]: units 1, 4, 16, 64
+        float a[4];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            a[u] = dot2_first(h[u][0], xp[u].x);
+            a[u + 2] = dot2_first(h[u][1], xp[u].y);
+            a[u] = dot2(h[u][2], xp[u].z, a[u]);
+            a[u + 2] = dot2(h[u][3], xp[u].w, a[u + 2]);
+            a[u] = dot2(h[u + 2][0], xp[u + 2].x, a[u]);
+            a[u + 2] = dot2(h[u + 2][1], xp[u + 2].y, a[u + 2]);
+            a[u] = dot2(h[u + 2][2], xp[u + 2].z, a[u]);
+            a[u + 2] = dot2(h[u + 2][3], xp[u + 2].w, a[u + 2]);
+        }
+        return __builtin_fmaf(a[3], 0.015625f,
+                              __builtin_fmaf(a[2], 0.0625f, __builtin_fmaf(a[1], 0.25f, a[0])));
+    } else {
         float ae = dot2_first(h[0][0], xp[0].x);
         float ao = dot2_first(h[0][1], xp[0].y);
         ae = dot2(h[0][2], xp[0].z, ae);
@@ -202,19 +211,6 @@ __device__ __forceinline__ float chunk_dot(const uint32_t (&h)[4][4], const uint
             ao = dot2(h[J][3], xp[J].w, ao);
         }
         return __builtin_fmaf(ao, 0.0625f, ae);
-    } else {
-        float a0 = dot2_first(h[0][0], xp[0].x);
-        float a1 = dot2_first(h[0][1], xp[0].y);
-        float a2 = dot2_first(h[0][2], xp[0].z);
-        float a3 = dot2_first(h[0][3], xp[0].w);
-#pragma unroll
-        for (int J = 1; J < 4; J++) {
-            a0 = dot2(h[J][0], xp[J].x, a0);
-            a1 = dot2(h[J][1], xp[J].y, a1);
-            a2 = dot2(h[J][2], xp[J].z, a2);
-            a3 = dot2(h[J][3], xp[J].w, a3);
-        }
-        return __builtin_fmaf(a3, 0.015625f, __builtin_fmaf(a2, 0.0625f, __builtin_fmaf(a1, 0.25f, a0)));
     }
 }
 

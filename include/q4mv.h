@@ -207,12 +207,12 @@ int q4mv_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo,
  * The low-bit code is the 4-bit code's top bits, q = q4 >> (4 - bits), as fn_q2_rows_h and
  * fn_q3_rows_h on the Constant BATCH_MSL page define them (codes q4 >> 2 and q4 >> 1). Each
  * 32-code chunk c of a row holds column t = 16i + 8u + p (i, u < 2, p < 8):
- *   Q2: q at bit (p < 4 ? 0 : 16) + 2(4u + p%4) of word 2c + i (2 words per chunk);
- *   Q3: q >> 1 at that bit of word 2c + i, and q & 1 at bit (p < 4 ? 0 : 16) + 8u + 2(p%4) + i
- *       of word 2C + c, C = in_dim/32 (a row is its 2C upper-bit words, then its C
- *       lowest-bit words: the two planes of fn_q3_rows_h).
- * A row is C*bits words. (The placement puts each code in the f16 lane of the activation
- * pair it multiplies, like the masked casts of those kernels.)
+ *   Q2: q at bit 4p + 2u of word 2c + i (2 words per chunk);
+ *   Q3: q >> 1 at that bit of word 2c + i, and q & 1 at bit 4p + 2i + u of word 2C + c,
+ *       C = in_dim/32 (a row is its 2C upper-bit words, then its C lowest-bit words: the
+ *       two planes of fn_q3_rows_h).
+ * A row is C*bits words. (Every code sits in the nibble of its column within its 8-column
+ * word, so one shift and one mask per word give the Q4 nibble layout.)
  *   codes : u8  [n_rows][in_dim]          one 4-bit code per byte (bits 4..7 ignored)
  *   w     : u32 [n_rows][in_dim/32*bits]  output (n_rows = n_mat * out_dim)
  * Errors: NULL pointer; bits not 2 or 3 (VALUE); n_rows < 1, in_dim < 64, in_dim % 64 != 0,

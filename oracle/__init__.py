@@ -259,11 +259,12 @@ def gemv_lowbit(bits, codes, scales, biases, x, rows=None):
 def pack_lowbit(bits, codes):
     """The packed low-bit words of 4-bit codes u8 [n_rows][in] -> u32 [n_rows][in/32*bits].
     Per 32-code chunk c, column t = 16i + 8u + p (i, u < 2, p < 8) holds q = q4 >> (4-bits):
-    Q2: q at bit (p < 4 ? 0 : 16) + 2(4u + p%4) of word 2c+i;
-    Q3: q >> 1 at that bit of word 2c+i, and q & 1 at bit (p < 4 ? 0 : 16) + 8u + 2(p%4) + i
-    of word 2C+c (C = in/32: the row's upper-bit words, then its lowest-bit words).
-    The placement puts each code where a mask lands it in the f16 lane of the activation pair
-    it multiplies (the masked casts of fn_q2_rows_h / fn_q3_rows_h)."""
+    Q2: q at bit 4p + 2u of word 2c+i;
+    Q3: q >> 1 at that bit of word 2c+i, and q & 1 at bit 4p + 2i + u of word 2C+c (C = in/32:
+    the row's upper-bit words, then its lowest-bit words).
+    Column t's field sits in nibble p of the word that (shifted by 2u) lines up with the
+    8 columns 16i + 8u + 0..7: one shift and one mask give a chunk's codes per nibble, and
+    per f16 lane pair (p, p + 4) in place."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     n, k = codes.shape
     C = k // 32
@@ -272,13 +273,12 @@ def pack_lowbit(bits, codes):
     low = np.zeros((n, C), dtype=np.uint32)
     for t in range(32):
         i, u, p = t // 16, (t // 8) % 2, t % 8
-        half = 0 if p < 4 else 16
-        pos = half + 2 * (4 * u + p % 4)
+        pos = 4 * p + 2 * u
         if bits == 2:
             up[:, :, i] |= q[:, :, t] << pos
         else:
             up[:, :, i] |= (q[:, :, t] >> 1) << pos
-            low |= (q[:, :, t] & 1) << (half + 8 * u + 2 * (p % 4) + i)
+            low |= (q[:, :, t] & 1) << (4 * p + 2 * i + u)
     if bits == 2:
         return up.reshape(n, 2 * C)
     return np.concatenate([up.reshape(n, 2 * C), low], axis=1)

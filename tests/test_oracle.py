@@ -565,14 +565,15 @@ def test_combine_closed_forms(oracle_lib):
 # ---- low-bit variants (Q2 / Q3)
 
 # (column within a 64-code row, word index, bit) written out by hand from the placement rule:
-# column t of chunk c meets activation pair (x_t, x_t+4) of its 8-column word, so columns
-# t and t+4 share one field position in the two 16-bit halves of a word.
-Q2_PROBES = [(0, 0, 0), (1, 0, 2), (3, 0, 6), (4, 0, 16), (7, 0, 22), (8, 0, 8), (11, 0, 14),
-             (12, 0, 24), (15, 0, 30), (16, 1, 0), (20, 1, 16), (24, 1, 8), (31, 1, 30),
-             (32, 2, 0), (45, 2, 26), (63, 3, 30)]
+# column t = 16i + 8u + p of chunk c sits in nibble p of word 2c + i shifted by 2u (bit
+# 4p + 2u), so columns t and t + 4 lie 16 bits apart (the two f16 halves of one lane); the
+# lowest bits of Q3 sit at bit 4p + 2i + u of the chunk's low-bit word.
+Q2_PROBES = [(0, 0, 0), (1, 0, 4), (3, 0, 12), (4, 0, 16), (7, 0, 28), (8, 0, 2), (11, 0, 14),
+             (12, 0, 18), (15, 0, 30), (16, 1, 0), (20, 1, 16), (24, 1, 2), (31, 1, 30),
+             (32, 2, 0), (45, 2, 22), (63, 3, 30)]
 # lowest-bit word of chunk c is word 2C + c (C = 2 here: words 4 and 5)
-Q3_LOW_PROBES = [(0, 4, 0), (4, 4, 16), (8, 4, 8), (13, 4, 26), (16, 4, 1), (20, 4, 17),
-                 (25, 4, 11), (31, 4, 31), (32, 5, 0), (63, 5, 31)]
+Q3_LOW_PROBES = [(0, 4, 0), (4, 4, 16), (8, 4, 1), (13, 4, 21), (16, 4, 2), (20, 4, 18),
+                 (25, 4, 7), (31, 4, 31), (32, 5, 0), (63, 5, 31)]
 
 
 def test_lowbit_pack_probes(oracle_lib):
