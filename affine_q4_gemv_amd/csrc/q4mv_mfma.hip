@@ -98,6 +98,12 @@
 #ifndef Q4MV_MFMA_BLOCKS_PER_CU
 #define Q4MV_MFMA_BLOCKS_PER_CU 4
 #endif
+// Short launches (K-split above 2: one block per CU, registers to spare): each thread loads
+// its first XPRE words of f32 activations before its weight loads. A wave's loads complete
+// in issue order, so staging loads issued after the weight loads wait for them.
+#ifndef Q4MV_MFMA_XPRE
+#define Q4MV_MFMA_XPRE 6
+#endif
 
 namespace q4mv_impl {
 
@@ -227,10 +233,23 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     // lanes one group (words per row are a multiple of 8). With xf_glu the rows are
     // [gate | up] and the values silu(gate) * up (as q4mv_swiglu_prep forms them). Returns
     // whether this thread saw an |x| of 4096 or more.
+    const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
+    const int rs4 = xf_glu ? in_full >> 1 : in_full >> 2;  // float4 per row
+    const float4 *const xf_m =
+        xf ? reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4 : nullptr;
+    // word (r, kw) of the plain f32 rows (rows past nb read row nb - 1)
+    auto fword_ptr = [&](int r, int kw) __attribute__((always_inline)) {
+        return xf_m + (size_t)min(r, nb - 1) * rs4 + 2 * ((k0 >> 3) + kw);
+    };
+    // the words loaded ahead of the weight loads (short launches, plain f32 rows)
+    // (not in 6-wave blocks: their registers would keep two blocks off one compute unit,
+    // which the 640- and 768-column expert rows need; 10- and 12-wave blocks need at most 4)
+    constexpr int kXPre = KS <= 2 || WPB == 6 ? 0
+                          : WPB >= 10 && Q4MV_MFMA_XPRE > 4 ? 4 : Q4MV_MFMA_XPRE;
+    const bool xpre_on = kXPre > 0 && xf && !xf_glu;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 xpre[kXPre > 0 ? kXPre : 1][2];
     auto fstage = [&](bool up) __attribute__((always_inline)) {
-        const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
-        const int rs4 = xf_glu ? in_full >> 1 : in_full >> 2;  // float4 per row
-        const float4 *xf_m = reinterpret_cast<const float4 *>(xf) + xrow0 * (size_t)rs4;
         float *xsw = reinterpret_cast<float *>(xsg_w);
         const half2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
         const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
@@ -274,9 +293,9 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
                 __attribute__((always_inline)) {
 #pragma unroll
                 for (int i = 0; i < 2; i++) {
-                    const float4 *row = xf_m + (size_t)min(r[i], nb - 1) * rs4;
-                    v[i][0] = row[2 * ((k0 >> 3) + kw[i])];
-                    v[i][1] = row[2 * ((k0 >> 3) + kw[i]) + 1];
+                    const float4 *p = fword_ptr(r[i], kw[i]);
+                    v[i][0] = p[0];
+                    v[i][1] = p[1];
                 }
             };
             auto fput = [&](const int (&r)[2], const int (&kw)[2], const float4 (&v)[2][2])
@@ -303,6 +322,19 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
             int ra[2], ka[2], rb[2], kb2[2];
             ra[0] = threadIdx.x / wrow;
             ka[0] = threadIdx.x - ra[0] * wrow;
+            if (up && xpre_on) {
+                // the words loaded ahead first, then the rest in rounds
+#pragma unroll
+                for (int i = 0; i < kXPre; i++) {
+                    if (ra[0] < nb) {  // uniform per 8 lanes
+                        const float f[8] = {xpre[i][0].x, xpre[i][0].y, xpre[i][0].z,
+                                            xpre[i][0].w, xpre[i][1].x, xpre[i][1].y,
+                                            xpre[i][1].z, xpre[i][1].w};
+                        fword(ra[0], ka[0], f);
+                    }
+                    adv(ra[0], ka[0]);
+                }
+            }
             ra[1] = ra[0];
             ka[1] = ka[0];
             adv(ra[1], ka[1]);
@@ -409,7 +441,9 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     // Each wave writes its own vote (so nothing needs clearing first); after the barrier
     // every thread reads all of them.
     auto stage = [&]() __attribute__((always_inline)) {
-        if (threadIdx.x < 8) zero_units[threadIdx.x] = 0;
+        if constexpr (kXPre == 0) {
+            if (threadIdx.x < 8) zero_units[threadIdx.x] = 0;
+        }
         const int mine = __any(xf ? fstage(true) : pstage(true)) ? 1 : 0;
         if ((threadIdx.x & 63) == 0) vote[threadIdx.x >> 6] = mine;
         __syncthreads();
@@ -632,10 +666,42 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     };
     u32x4 c0[4], c1[4];
     SbRegs s0, s1;
+    if constexpr (kXPre > 0) {
+        if (threadIdx.x < 8) zero_units[threadIdx.x] = 0;  // read after the staging barrier
+    }
+    if (xpre_on) {
+        // Issued ahead of the weight loads (a wave's loads complete in issue order, so they
+        // wait for nothing else), only as many rounds as the block's words need (uniform).
+        // Unconditional within a round (words past the rows re-read row nb - 1), so no
+        // branch invites the compiler to convert, and wait for, a word before the next
+        // load is issued.
+        const int npre = min(kXPre, (words + TH - 1) / TH);
+        int r = threadIdx.x / wrow, kw = threadIdx.x - r * wrow;
+#pragma unroll
+        for (int i = 0; i < kXPre; i++) {
+            if (i < npre) {
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(fword_ptr(min(r, nb - 1), kw));
+                xpre[i][0] = p[0];
+                xpre[i][1] = p[1];
+            }
+            adv(r, kw);
+        }
+    }
     // the first tile's scale block (visible to the tile group after the staging barrier)
     tb_load(base + slot);  // (a tile past the end re-reads the last one: unused)
-    if (more(abase)) load(abase + slot, unit_quad(aui), aui, c0, s0);
+    // With words loaded ahead the first unit's loads are unconditional (a tile past the end
+    // re-reads the last tile's rows, unused), so the waits below know which loads follow
+    // the words on every path.
+    if (kXPre > 0 || more(abase)) load(abase + slot, unit_quad(aui), aui, c0, s0);
     advance(abase, aui);
+    // The words loaded ahead are used from here on (the empty asm statements: the compiler
+    // waits for them here, with only the first unit's loads issued after them, and not
+    // later, where loads issued on only some paths would make it wait for weights too).
+    // The next unit's loads follow. (Ahead of that wait, they measured slower: its waits
+    // then also covered the first unit's loads on some paths.)
+#pragma unroll
+    for (int i = 0; i < kXPre; i++)
+        asm volatile("; staged words" : "+v"(xpre[i][0]), "+v"(xpre[i][1]));
     if (more(abase)) load(abase + slot, unit_quad(aui), aui, c1, s1);
     advance(abase, aui);
     if (more(base)) tb_store();
