@@ -146,7 +146,8 @@ __device__ __forceinline__ u32x4 lowbit_to_q4(const u32x4 v)
 // first unit of a part) and kept in the scratch for the next (groups % 8 == 0, 16-byte
 // aligned arrays; halves the scattered scale loads); 8 = one aligned 8-byte load per quad
 // (groups % 4 == 0, 8-byte aligned); 2 = four 2-byte loads with clamped indices.
-template <int WPB, int KS, bool NB16, int SBW, bool MF16, int BITS = 4, bool R8 = false>
+template <int WPB, int KS, bool NB16, int SBW, bool MF16, int BITS = 4, bool R8 = false,
+          bool XPRE = false>
 __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 : 1) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
@@ -241,11 +242,13 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     auto fword_ptr = [&](int r, int kw) __attribute__((always_inline)) {
         return xf_m + (size_t)min(r, nb - 1) * rs4 + 2 * ((k0 >> 3) + kw);
     };
-    // the words loaded ahead of the weight loads (short launches, plain f32 rows): 10- and
+    // the words loaded ahead of the weight loads (short launches, plain f32 rows: the XPRE
+    // instances; the others keep the staging after the weight loads, which measured faster
+    // from the prepared streams, 2560 x 2560 NB 4 6.22 against 6.43 us): 10- and
     // 12-wave blocks need at most 4 per thread; 6-wave blocks (640- and 768-column expert
     // rows) take 2, which keeps their registers within four waves per SIMD, so that two
     // blocks share a compute unit (8 x 2560 x 640 NB 4 6.92 -> 6.71 us, NB 8 7.17 -> 6.97)
-    constexpr int kXPre = KS <= 2 ? 0 : WPB == 6 ? 2
+    constexpr int kXPre = !XPRE || KS <= 2 ? 0 : WPB == 6 ? 2
                           : WPB >= 10 && Q4MV_MFMA_XPRE > 4 ? 4 : Q4MV_MFMA_XPRE;
     const bool xpre_on = kXPre > 0 && xf && !xf_glu;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -927,14 +930,14 @@ static bool use_mf16(int ks, int nb, long tiles)
            (nb <= 4 || nb > 8 || Q4MV_MFMA_MF16_R8);
 }
 
-template <int WPB, int KS, bool NB16, bool MF16, bool R8 = false>
+template <int WPB, int KS, bool NB16, bool MF16, bool R8 = false, bool XPRE = false>
 static MfmaFn pick_sb(int sbw)
 {
     if constexpr (KS == 2 && (WPB == kMfmaWaves || (Q4MV_MFMA_NB8_WPB4 && WPB == 4)))
         if (sbw == 32) return mfma_kernel<WPB, KS, NB16, 32, MF16, 4, R8>;
-    return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16, MF16, 4, R8>
-           : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8, MF16, 4, R8>
-                      : mfma_kernel<WPB, KS, NB16, 2, MF16, 4, R8>;
+    return sbw == 16 ? mfma_kernel<WPB, KS, NB16, 16, MF16, 4, R8, XPRE>
+           : sbw == 8 ? mfma_kernel<WPB, KS, NB16, 8, MF16, 4, R8, XPRE>
+                      : mfma_kernel<WPB, KS, NB16, 2, MF16, 4, R8, XPRE>;
 }
 
 // Low-bit codes: 8-wave blocks and 8- or 16-byte scale loads only (q4mv_lowbit checks).
@@ -979,8 +982,13 @@ static MfmaFn pick_lowbit(int ks, bool nb16, int sbw, bool mf16, bool r8)
 }
 
 template <int WPB, int KS>
-static MfmaFn pick(bool nb16, int sbw, bool mf16, bool r8)
+static MfmaFn pick(bool nb16, int sbw, bool mf16, bool r8, bool xpre)
 {
+    // short launches staging plain f32 rows: the instances that load them ahead
+    if constexpr (KS > 2)
+        if (xpre)
+            return nb16 ? pick_sb<WPB, KS, true, false, false, true>(sbw)
+                        : pick_sb<WPB, KS, false, false, false, true>(sbw);
     // the 16x16x32 path covers 16 activation rows either way; nb > 8 gets an instance of its
     // own so that the register cap for two blocks per CU (tile-block scales, nb <= 8) does
     // not apply where the LDS allows only one
@@ -1088,6 +1096,7 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
     const bool mf16 = use_mf16(sh.ks, a.nb, tiles);
     const bool r8 = mf16 && a.nb > 4 && a.nb <= 8;  // 16x16x32 with two 8-row group slots
+    const bool xpre = a.xf != nullptr && !a.xf_glu;  // plain f32 rows staged in the launch
     const size_t lds0 = mfma_lds_bytes(klen, a.nb) + part_bytes(sh.wpb, sh.ks, a.nb, tiles);
     // 16-byte scale loads when the layout allows and their larger scratch still fits (every
     // row's slice of scales must start on an 8- or 16-byte boundary)
@@ -1120,19 +1129,19 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
                              : pick_lowbit<3>(sh.ks, nb16, sbw, mf16, r8);
     } else {
         switch (wk) {
-        case 801: fn = pick<8, 1>(nb16, sbw, mf16, r8); break;
-        case 802: fn = pick<8, 2>(nb16, sbw, mf16, r8); break;
-        case 804: fn = pick<8, 4>(nb16, sbw, mf16, r8); break;
-        case 808: fn = pick<8, 8>(nb16, sbw, mf16, r8); break;
-        case 401: fn = pick<4, 1>(nb16, sbw, mf16, r8); break;
-        case 402: fn = pick<4, 2>(nb16, sbw, mf16, r8); break;
-        case 404: fn = pick<4, 4>(nb16, sbw, mf16, r8); break;
+        case 801: fn = pick<8, 1>(nb16, sbw, mf16, r8, xpre); break;
+        case 802: fn = pick<8, 2>(nb16, sbw, mf16, r8, xpre); break;
+        case 804: fn = pick<8, 4>(nb16, sbw, mf16, r8, xpre); break;
+        case 808: fn = pick<8, 8>(nb16, sbw, mf16, r8, xpre); break;
+        case 401: fn = pick<4, 1>(nb16, sbw, mf16, r8, xpre); break;
+        case 402: fn = pick<4, 2>(nb16, sbw, mf16, r8, xpre); break;
+        case 404: fn = pick<4, 4>(nb16, sbw, mf16, r8, xpre); break;
 #if Q4MV_MFMA_KSQ
-        case 603: fn = pick<6, 3>(nb16, sbw, mf16, r8); break;
-        case 1005: fn = pick<10, 5>(nb16, sbw, mf16, r8); break;
-        case 1206: fn = pick<12, 6>(nb16, sbw, mf16, r8); break;
-        case 1010: fn = pick<10, 10>(nb16, sbw, mf16, r8); break;
-        case 1212: fn = pick<12, 12>(nb16, sbw, mf16, r8); break;
+        case 603: fn = pick<6, 3>(nb16, sbw, mf16, r8, xpre); break;
+        case 1005: fn = pick<10, 5>(nb16, sbw, mf16, r8, xpre); break;
+        case 1206: fn = pick<12, 6>(nb16, sbw, mf16, r8, xpre); break;
+        case 1010: fn = pick<10, 10>(nb16, sbw, mf16, r8, xpre); break;
+        case 1212: fn = pick<12, 12>(nb16, sbw, mf16, r8, xpre); break;
 #endif
         default: break;
         }
