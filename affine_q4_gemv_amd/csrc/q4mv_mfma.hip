@@ -242,7 +242,7 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     auto fword_ptr = [&](int r, int kw) __attribute__((always_inline)) {
         return xf_m + (size_t)min(r, nb - 1) * rs4 + 2 * ((k0 >> 3) + kw);
     };
-    // the words loaded ahead of the weight loads (short launches, plain f32 rows: the XPRE
+    // the words loaded ahead of the weight loads (short launches, f32 rows: the XPRE
     // instances; the others keep the staging after the weight loads, which measured faster
     // from the prepared streams, 2560 x 2560 NB 4 6.22 against 6.43 us): 10- and
     // 12-wave blocks need at most 4 per thread; 6-wave blocks (640- and 768-column expert
@@ -251,6 +251,9 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     constexpr int kXPre = !XPRE || KS <= 2 ? 0 : WPB == 6 ? 2
                           : WPB >= 10 && Q4MV_MFMA_XPRE > 4 ? 4 : Q4MV_MFMA_XPRE;
     const bool xpre_on = kXPre > 0 && xf && !xf_glu;
+    // [gate | up] rows: a word is two pairs of float4 (gate, up), kept in two entries
+    constexpr int kXPreGlu = kXPre / 2;
+    const bool xpre_glu = kXPreGlu > 0 && xf && xf_glu;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x4 xpre[kXPre > 0 ? kXPre : 1][2];
     auto fstage = [&](bool up) __attribute__((always_inline)) {
@@ -281,8 +284,27 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
             lds[r * RS + kw] = u;
         };
         if (xf_glu) {
-            // [gate | up] rows: one word per thread at a time
-            for (int wi = threadIdx.x; wi < words; wi += TH) {  // uniform per 8 lanes
+            // [gate | up] rows: one word per thread at a time (the words loaded ahead first)
+            int wi = threadIdx.x;
+            if (up && xpre_glu) {
+#pragma unroll
+                for (int i = 0; i < kXPreGlu; i++) {
+                    if (wi < words) {  // uniform per 8 lanes
+                        const int r = wi / wrow, kw = wi - r * wrow;
+                        const f32x4 g0 = xpre[2 * i][0], g1 = xpre[2 * i][1];
+                        const f32x4 u0 = xpre[2 * i + 1][0], u1 = xpre[2 * i + 1][1];
+                        const float4 v[4] = {{g0[0], g0[1], g0[2], g0[3]},
+                                             {g1[0], g1[1], g1[2], g1[3]},
+                                             {u0[0], u0[1], u0[2], u0[3]},
+                                             {u1[0], u1[1], u1[2], u1[3]}};
+                        float f[8];
+                        xword_values(v, 1, f);
+                        fword(r, kw, f);
+                    }
+                    wi += TH;
+                }
+            }
+            for (; wi < words; wi += TH) {  // uniform per 8 lanes
                 const int r = wi / wrow, kw = wi - r * wrow;
                 float4 v[4];
                 xword_load(xf_m + (size_t)r * rs4, (k0 >> 3) + kw, in_full, 1, v);
@@ -690,6 +712,22 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
             }
             adv(r, kw);
         }
+    } else if (xpre_glu) {
+        // [gate | up] words, as fstage's loop takes them (a clamped row past nb)
+        const int npre = min(kXPreGlu, (words + TH - 1) / TH);
+        int r = threadIdx.x / wrow, kw = threadIdx.x - r * wrow;
+#pragma unroll
+        for (int i = 0; i < kXPreGlu; i++) {
+            if (i < npre) {
+                float4 v[4];
+                xword_load(xf_m + (size_t)min(r, nb - 1) * rs4, (k0 >> 3) + kw, in_full, 1, v);
+                xpre[2 * i][0] = f32x4{v[0].x, v[0].y, v[0].z, v[0].w};
+                xpre[2 * i][1] = f32x4{v[1].x, v[1].y, v[1].z, v[1].w};
+                xpre[2 * i + 1][0] = f32x4{v[2].x, v[2].y, v[2].z, v[2].w};
+                xpre[2 * i + 1][1] = f32x4{v[3].x, v[3].y, v[3].z, v[3].w};
+            }
+            adv(r, kw);
+        }
     }
     // the first tile's scale block (visible to the tile group after the staging barrier)
     tb_load(base + slot);  // (a tile past the end re-reads the last one: unused)
@@ -984,7 +1022,7 @@ static MfmaFn pick_lowbit(int ks, bool nb16, int sbw, bool mf16, bool r8)
 template <int WPB, int KS>
 static MfmaFn pick(bool nb16, int sbw, bool mf16, bool r8, bool xpre)
 {
-    // short launches staging plain f32 rows: the instances that load them ahead
+    // short launches staging f32 rows: the instances that load them ahead
     if constexpr (KS > 2)
         if (xpre)
             return nb16 ? pick_sb<WPB, KS, true, false, false, true>(sbw)
@@ -1096,7 +1134,7 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
     const bool mf16 = use_mf16(sh.ks, a.nb, tiles);
     const bool r8 = mf16 && a.nb > 4 && a.nb <= 8;  // 16x16x32 with two 8-row group slots
-    const bool xpre = a.xf != nullptr && !a.xf_glu;  // plain f32 rows staged in the launch
+    const bool xpre = a.xf != nullptr;  // f32 rows staged in the launch
     const size_t lds0 = mfma_lds_bytes(klen, a.nb) + part_bytes(sh.wpb, sh.ks, a.nb, tiles);
     // 16-byte scale loads when the layout allows and their larger scratch still fits (every
     // row's slice of scales must start on an 8- or 16-byte boundary)
