@@ -147,7 +147,7 @@ __device__ __forceinline__ u32x4 lowbit_to_q4(const u32x4 v)
 // aligned arrays; halves the scattered scale loads); 8 = one aligned 8-byte load per quad
 // (groups % 4 == 0, 8-byte aligned); 2 = four 2-byte loads with clamped indices.
 template <int WPB, int KS, bool NB16, int SBW, bool MF16, int BITS = 4, bool R8 = false,
-          bool XPRE = false>
+          int XPRE = 0>
 __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 : 1) void mfma_kernel(
     const uint4 *__restrict__ w, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint2 *__restrict__ xe,
@@ -242,19 +242,24 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     auto fword_ptr = [&](int r, int kw) __attribute__((always_inline)) {
         return xf_m + (size_t)min(r, nb - 1) * rs4 + 2 * ((k0 >> 3) + kw);
     };
-    // the words loaded ahead of the weight loads (short launches, f32 rows: the XPRE
-    // instances; the others keep the staging after the weight loads, which measured faster
-    // from the prepared streams, 2560 x 2560 NB 4 6.22 against 6.43 us): 10- and
-    // 12-wave blocks need at most 4 per thread; 6-wave blocks (640- and 768-column expert
-    // rows) take 2, which keeps their registers within four waves per SIMD, so that two
-    // blocks share a compute unit (8 x 2560 x 640 NB 4 6.92 -> 6.71 us, NB 8 7.17 -> 6.97)
-    constexpr int kXPre = !XPRE || KS <= 2 ? 0 : WPB == 6 ? 2
-                          : WPB >= 10 && Q4MV_MFMA_XPRE > 4 ? 4 : Q4MV_MFMA_XPRE;
-    const bool xpre_on = kXPre > 0 && xf && !xf_glu;
-    // [gate | up] rows: a word is two pairs of float4 (gate, up), kept in two entries
-    constexpr int kXPreGlu = kXPre / 2;
+    // The words loaded ahead of the weight loads on short launches staging f32 rows: XPRE
+    // 1 (plain rows) and 2 ([gate | up] rows) instances; XPRE 0 keeps the staging after the
+    // weight loads, which measured faster from the prepared streams (2560 x 2560 NB 4 6.22
+    // against 6.43 us). Plain rows: up to 6 words per thread in 8-wave blocks, 4 in 10- and
+    // 12-wave blocks (all they need at nb <= 8), 1 in 6-wave blocks (640- and 768-column
+    // expert rows), where more registers would keep two blocks off one compute unit
+    // (8 x 2560 x 640 NB 4 6.90 -> 6.70 us). [gate | up] rows: a word takes two entries
+    // (gate, up): 3, 2 and 1 words.
+    constexpr int kXPreWords = XPRE != 1 || KS <= 2 ? 0 : WPB == 6 ? 1
+                               : WPB >= 10 && Q4MV_MFMA_XPRE > 4 ? 4 : Q4MV_MFMA_XPRE;
+    constexpr int kXPreGlu = XPRE != 2 || KS <= 2 ? 0 : WPB == 6 ? 1
+                             : WPB >= 10 && Q4MV_MFMA_XPRE > 4 ? 2 : Q4MV_MFMA_XPRE / 2;
+    constexpr int kXPre = XPRE == 2 ? 2 * kXPreGlu : kXPreWords;  // register entries
+    const bool xpre_on = kXPreWords > 0 && xf && !xf_glu;
     const bool xpre_glu = kXPreGlu > 0 && xf && xf_glu;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
+    // (entries a thread does not load are zeroed: they still pass through the asm
+    // statements below, and are never read after them)
     f32x4 xpre[kXPre > 0 ? kXPre : 1][2];
     auto fstage = [&](bool up) __attribute__((always_inline)) {
         float *xsw = reinterpret_cast<float *>(xsg_w);
@@ -351,7 +356,7 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
             if (up && xpre_on) {
                 // the words loaded ahead first, then the rest in rounds
 #pragma unroll
-                for (int i = 0; i < kXPre; i++) {
+                for (int i = 0; i < kXPreWords; i++) {
                     if (ra[0] < nb) {  // uniform per 8 lanes
                         const float f[8] = {xpre[i][0].x, xpre[i][0].y, xpre[i][0].z,
                                             xpre[i][0].w, xpre[i][1].x, xpre[i][1].y,
@@ -701,14 +706,16 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
         // Unconditional within a round (words past the rows re-read row nb - 1), so no
         // branch invites the compiler to convert, and wait for, a word before the next
         // load is issued.
-        const int npre = min(kXPre, (words + TH - 1) / TH);
+        const int npre = min(kXPreWords, (words + TH - 1) / TH);
         int r = threadIdx.x / wrow, kw = threadIdx.x - r * wrow;
 #pragma unroll
-        for (int i = 0; i < kXPre; i++) {
+        for (int i = 0; i < kXPreWords; i++) {
             if (i < npre) {
                 const f32x4 *p = reinterpret_cast<const f32x4 *>(fword_ptr(min(r, nb - 1), kw));
                 xpre[i][0] = p[0];
                 xpre[i][1] = p[1];
+            } else {
+                xpre[i][0] = xpre[i][1] = f32x4{};
             }
             adv(r, kw);
         }
@@ -725,9 +732,15 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
                 xpre[2 * i][1] = f32x4{v[1].x, v[1].y, v[1].z, v[1].w};
                 xpre[2 * i + 1][0] = f32x4{v[2].x, v[2].y, v[2].z, v[2].w};
                 xpre[2 * i + 1][1] = f32x4{v[3].x, v[3].y, v[3].z, v[3].w};
+            } else {
+                xpre[2 * i][0] = xpre[2 * i][1] = f32x4{};
+                xpre[2 * i + 1][0] = xpre[2 * i + 1][1] = f32x4{};
             }
             adv(r, kw);
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kXPre; i++) xpre[i][0] = xpre[i][1] = f32x4{};
     }
     // the first tile's scale block (visible to the tile group after the staging barrier)
     tb_load(base + slot);  // (a tile past the end re-reads the last one: unused)
@@ -968,7 +981,7 @@ static bool use_mf16(int ks, int nb, long tiles)
            (nb <= 4 || nb > 8 || Q4MV_MFMA_MF16_R8);
 }
 
-template <int WPB, int KS, bool NB16, bool MF16, bool R8 = false, bool XPRE = false>
+template <int WPB, int KS, bool NB16, bool MF16, bool R8 = false, int XPRE = 0>
 static MfmaFn pick_sb(int sbw)
 {
     if constexpr (KS == 2 && (WPB == kMfmaWaves || (Q4MV_MFMA_NB8_WPB4 && WPB == 4)))
@@ -1020,22 +1033,36 @@ static MfmaFn pick_lowbit(int ks, bool nb16, int sbw, bool mf16, bool r8)
 }
 
 template <int WPB, int KS>
-static MfmaFn pick(bool nb16, int sbw, bool mf16, bool r8, bool xpre)
+static MfmaFn pick(bool nb16, int sbw, bool mf16, bool r8, int xmode)
 {
-    // short launches staging f32 rows: the instances that load them ahead
-    if constexpr (KS > 2)
-        if (xpre)
-            return nb16 ? pick_sb<WPB, KS, true, false, false, true>(sbw)
-                        : pick_sb<WPB, KS, false, false, false, true>(sbw);
-    // the 16x16x32 path covers 16 activation rows either way; nb > 8 gets an instance of its
-    // own so that the register cap for two blocks per CU (tile-block scales, nb <= 8) does
-    // not apply where the LDS allows only one
-    if constexpr (KS <= 2)
-        if (mf16)
-            return nb16 ? pick_sb<WPB, KS, true, true>(sbw)
-                   : r8 ? pick_sb<WPB, KS, false, true, true>(sbw)
-                        : pick_sb<WPB, KS, false, true>(sbw);
-    return nb16 ? pick_sb<WPB, KS, true, false>(sbw) : pick_sb<WPB, KS, false, false>(sbw);
+    // one quad per wave (K-split 3, 5, 6, 10 or 12): chosen for nb <= 8 only, on 32x32x16
+    constexpr bool kOneQuad = KS > 2 && KS != 4 && KS != 8;
+    if constexpr (kOneQuad) {
+        if (nb16) return nullptr;
+        // short launches staging f32 rows (xmode 1 plain, 2 [gate | up]): the instances
+        // that load them ahead
+        if (xmode == 1) return pick_sb<WPB, KS, false, false, false, 1>(sbw);
+        if (xmode == 2) return pick_sb<WPB, KS, false, false, false, 2>(sbw);
+        return pick_sb<WPB, KS, false, false>(sbw);
+    } else {
+        if constexpr (KS > 2) {
+            if (xmode == 1)
+                return nb16 ? pick_sb<WPB, KS, true, false, false, 1>(sbw)
+                            : pick_sb<WPB, KS, false, false, false, 1>(sbw);
+            if (xmode == 2)
+                return nb16 ? pick_sb<WPB, KS, true, false, false, 2>(sbw)
+                            : pick_sb<WPB, KS, false, false, false, 2>(sbw);
+        }
+        // the 16x16x32 path covers 16 activation rows either way; nb > 8 gets an instance
+        // of its own so that the register cap for two blocks per CU (tile-block scales,
+        // nb <= 8) does not apply where the LDS allows only one
+        if constexpr (KS <= 2)
+            if (mf16)
+                return nb16 ? pick_sb<WPB, KS, true, true>(sbw)
+                       : r8 ? pick_sb<WPB, KS, false, true, true>(sbw)
+                            : pick_sb<WPB, KS, false, true>(sbw);
+        return nb16 ? pick_sb<WPB, KS, true, false>(sbw) : pick_sb<WPB, KS, false, false>(sbw);
+    }
 }
 
 // Partial-sum bytes of a launch shape: accumulators per lane, and the lanes that hold
@@ -1134,7 +1161,7 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
     if (sh.wpb == 0) return hipErrorInvalidValue;  // rejected on the host before this point
     const bool mf16 = use_mf16(sh.ks, a.nb, tiles);
     const bool r8 = mf16 && a.nb > 4 && a.nb <= 8;  // 16x16x32 with two 8-row group slots
-    const bool xpre = a.xf != nullptr;  // f32 rows staged in the launch
+    const int xmode = !a.xf ? 0 : a.xf_glu ? 2 : 1;  // f32 rows staged in the launch
     const size_t lds0 = mfma_lds_bytes(klen, a.nb) + part_bytes(sh.wpb, sh.ks, a.nb, tiles);
     // 16-byte scale loads when the layout allows and their larger scratch still fits (every
     // row's slice of scales must start on an 8- or 16-byte boundary)
@@ -1167,19 +1194,19 @@ static hipError_t launch_mfma_slice(const GemvArgs &a, int k0, int klen, int acc
                              : pick_lowbit<3>(sh.ks, nb16, sbw, mf16, r8);
     } else {
         switch (wk) {
-        case 801: fn = pick<8, 1>(nb16, sbw, mf16, r8, xpre); break;
-        case 802: fn = pick<8, 2>(nb16, sbw, mf16, r8, xpre); break;
-        case 804: fn = pick<8, 4>(nb16, sbw, mf16, r8, xpre); break;
-        case 808: fn = pick<8, 8>(nb16, sbw, mf16, r8, xpre); break;
-        case 401: fn = pick<4, 1>(nb16, sbw, mf16, r8, xpre); break;
-        case 402: fn = pick<4, 2>(nb16, sbw, mf16, r8, xpre); break;
-        case 404: fn = pick<4, 4>(nb16, sbw, mf16, r8, xpre); break;
+        case 801: fn = pick<8, 1>(nb16, sbw, mf16, r8, xmode); break;
+        case 802: fn = pick<8, 2>(nb16, sbw, mf16, r8, xmode); break;
+        case 804: fn = pick<8, 4>(nb16, sbw, mf16, r8, xmode); break;
+        case 808: fn = pick<8, 8>(nb16, sbw, mf16, r8, xmode); break;
+        case 401: fn = pick<4, 1>(nb16, sbw, mf16, r8, xmode); break;
+        case 402: fn = pick<4, 2>(nb16, sbw, mf16, r8, xmode); break;
+        case 404: fn = pick<4, 4>(nb16, sbw, mf16, r8, xmode); break;
 #if Q4MV_MFMA_KSQ
-        case 603: fn = pick<6, 3>(nb16, sbw, mf16, r8, xpre); break;
-        case 1005: fn = pick<10, 5>(nb16, sbw, mf16, r8, xpre); break;
-        case 1206: fn = pick<12, 6>(nb16, sbw, mf16, r8, xpre); break;
-        case 1010: fn = pick<10, 10>(nb16, sbw, mf16, r8, xpre); break;
-        case 1212: fn = pick<12, 12>(nb16, sbw, mf16, r8, xpre); break;
+        case 603: fn = pick<6, 3>(nb16, sbw, mf16, r8, xmode); break;
+        case 1005: fn = pick<10, 5>(nb16, sbw, mf16, r8, xmode); break;
+        case 1206: fn = pick<12, 6>(nb16, sbw, mf16, r8, xmode); break;
+        case 1010: fn = pick<10, 10>(nb16, sbw, mf16, r8, xmode); break;
+        case 1212: fn = pick<12, 12>(nb16, sbw, mf16, r8, xmode); break;
 #endif
         default: break;
         }
