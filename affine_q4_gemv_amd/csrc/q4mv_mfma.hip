@@ -99,8 +99,9 @@
 #define Q4MV_MFMA_BLOCKS_PER_CU 4
 #endif
 // Short launches (K-split above 2: one block per CU, registers to spare): each thread loads
-// its first XPRE words of f32 activations before its weight loads. A wave's loads complete
-// in issue order, so staging loads issued after the weight loads wait for them.
+// its first words of f32 activations before its weight loads, at most Q4MV_MFMA_XPRE in
+// 8-wave blocks. A wave's loads complete in issue order, so staging loads issued after the
+// weight loads wait for them.
 #ifndef Q4MV_MFMA_XPRE
 #define Q4MV_MFMA_XPRE 6
 #endif
@@ -201,21 +202,14 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     // overflow), the block stages again with x (even) and x/16 (odd; exact for |x| >= 2^-10,
     // else rounded to the f16 subnormal spacing) and the store scales by 2^24. The choice
     // depends only on the staged rows, so every block of a matrix makes the same one.
-    // Fused prep (xf non-null: f32 activations): the f16 rounding and the chunk sums of
-    // q4mv_prepare_x done here with the same additions (pair sums, a balanced tree over a
-    // chunk's 16 pairs: each thread adds its word's four pairs, two quad DPP steps add the
-    // chunk's four words; then a group's two chunks in order), so the LDS contents are
-    // bitwise those staged from q4mv_prepare_x's outputs. One thread per 8-column word; a
-    // quad of lanes is one chunk, 8 lanes one group (words per row are a multiple of 8). With
-    // xf_glu the rows are [gate | up] and the values silu(gate) * up (as q4mv_swiglu_prep
-    // forms them). Returns whether this thread saw an |x| of 4096 or more.
     // Thread t takes words (units) t, t + TH, t + 2 TH, ... of the nb * in_dim / 8 staged
     // words; their row and column are advanced incrementally (no division per word). The
     // staging runs after each wave has issued its first weight loads, in rounds (2 words per
     // thread with f32 activations, 4 units with the prepared ones); the next round's loads
-    // are issued before the current round is converted and written. (Issuing the first
-    // rounds ahead of the weight loads measured slower: the registers they hold across those
-    // loads cost the LM head its second block per CU.)
+    // are issued before the current round is converted and written. On short launches
+    // staging f32 rows the first words are loaded ahead of the weight loads (xpre below); on
+    // the LM head's launches that measured slower (the registers they hold across those
+    // loads cost it its second block per CU).
     const int wrow = in_dim >> 3, words = nb * wrow;
     const int dr = TH / wrow, dk = TH - dr * wrow;  // advance by TH words
     auto adv = [&](int &r, int &kw) __attribute__((always_inline)) {
@@ -226,14 +220,6 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
             r++;
         }
     };
-    // Fused prep (xf non-null: f32 activations): the f16 rounding and the chunk sums of
-    // q4mv_prepare_x done here with the same additions (pair sums, a balanced tree over a
-    // chunk's 16 pairs: each thread adds its word's four pairs, two quad DPP steps add the
-    // chunk's four words; then a group's two chunks in order), so the LDS contents are
-    // bitwise those staged from q4mv_prepare_x's outputs. A quad of lanes is one chunk, 8
-    // lanes one group (words per row are a multiple of 8). With xf_glu the rows are
-    // [gate | up] and the values silu(gate) * up (as q4mv_swiglu_prep forms them). Returns
-    // whether this thread saw an |x| of 4096 or more.
     const size_t xrow0 = x_shared ? 0 : (size_t)m * nb;
     const int rs4 = xf_glu ? in_full >> 1 : in_full >> 2;  // float4 per row
     const float4 *const xf_m =
@@ -261,6 +247,14 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
     // (entries a thread does not load are zeroed: they still pass through the asm
     // statements below, and are never read after them)
     f32x4 xpre[kXPre > 0 ? kXPre : 1][2];
+    // Fused prep (xf non-null: f32 activations): the f16 rounding and the chunk sums of
+    // q4mv_prepare_x done here with the same additions (pair sums, a balanced tree over a
+    // chunk's 16 pairs: each thread adds its word's four pairs, two quad DPP steps add the
+    // chunk's four words; then a group's two chunks in order), so the LDS contents are
+    // bitwise those staged from q4mv_prepare_x's outputs. A quad of lanes is one chunk, 8
+    // lanes one group (words per row are a multiple of 8). With xf_glu the rows are
+    // [gate | up] and the values silu(gate) * up (as q4mv_swiglu_prep forms them). Returns
+    // whether this thread saw an |x| of 4096 or more.
     auto fstage = [&](bool up) __attribute__((always_inline)) {
         float *xsw = reinterpret_cast<float *>(xsg_w);
         const half2_t sixteen = {(_Float16)16.0f, (_Float16)16.0f};
