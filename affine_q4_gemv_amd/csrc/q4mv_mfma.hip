@@ -549,9 +549,15 @@ __global__ __launch_bounds__(WPB * 64, (MF16 && SBW == 32 && !NB16 && !R8) ? 4 :
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int row = narrow ? min(8 * r + lr8, out_dim - 1) : 8 * r + lr8;
-                const uint32_t *wr = wl_m + (size_t)(trow + row) * Cf * BITS;
-                const u32x2 up = *reinterpret_cast<const u32x2 *>(wr + 2 * (kc0 + chunk));
-                cw[r] = u32x4{up[0], up[1], BITS == 3 ? wr[2 * Cf + kc0 + chunk] : 0u, 0u};
+                // a chunk is BITS consecutive words (Q3: two upper-bit words, then the
+                // lowest-bit word)
+                const uint32_t *wr = wl_m + (size_t)(trow + row) * Cf * BITS + BITS * (kc0 + chunk);
+                if constexpr (BITS == 2) {
+                    const u32x2 up = *reinterpret_cast<const u32x2 *>(wr);
+                    cw[r] = u32x4{up[0], up[1], 0u, 0u};
+                } else {
+                    cw[r] = u32x4{wr[0], wr[1], wr[2], 0u};
+                }
             }
         }
 #pragma unroll

@@ -56,10 +56,12 @@ __global__ __launch_bounds__(256) void pack_lowbit_kernel(const uint4 *__restric
             low |= (q & 1u) << (4 * p + 2 * wi + u);
         }
     }
-    uint32_t *wr = w + row * C * BITS;
-    wr[2 * c] = word[0];
-    wr[2 * c + 1] = word[1];
-    if constexpr (BITS == 3) wr[2 * C + c] = low;
+    // a chunk is BITS consecutive words: Q2 its two words, Q3 its two upper-bit words, then
+    // its lowest-bit word
+    uint32_t *wr = w + row * C * BITS + (int64_t)c * BITS;
+    wr[0] = word[0];
+    wr[1] = word[1];
+    if constexpr (BITS == 3) wr[2] = low;
 }
 
 hipError_t launch_pack_lowbit(int bits, const uint8_t *codes, uint32_t *w, int64_t n_rows,

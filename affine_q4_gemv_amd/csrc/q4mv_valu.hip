@@ -114,14 +114,14 @@ constexpr int valu_sb_segs(int rows, int cpl, bool specialised)
 //      is the 2-bit field at bit 4p + 2u.
 //   Q3 upper words: the code's upper two bits at those positions; lowest-bit word of chunk c:
 //      the low bit of column 32c+16i+8u+p at bit 4p + 2i + u.
-// Row layout: Q4 C chunks of 4 words; Q2 C chunks of 2 words; Q3 the 2C upper words, then
-// the C lowest-bit words. So a row is C * BITS words in every case.
+// Row layout: C chunks of BITS words (Q4 4 words; Q2 2 words; Q3 its 2 upper-bit words, then
+// its lowest-bit word), so a row is C * BITS words and a chunk one contiguous load.
 
 // One chunk's code words of row base wr (u32 units), streamed with non-temporal loads
 // (each byte is used once). Q4: 4 words; Q2: 2 words (.x, .y); Q3: 2 upper words and the
-// lowest-bit word (.z).
+// lowest-bit word (.z), one 12-byte load.
 template <int BITS, bool NT>
-__device__ __forceinline__ uint4 load_chunk(const uint32_t *wr, int c, int C)
+__device__ __forceinline__ uint4 load_chunk(const uint32_t *wr, int c)
 {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -130,14 +130,18 @@ __device__ __forceinline__ uint4 load_chunk(const uint32_t *wr, int c, int C)
         const u32x4 v = NT ? __builtin_nontemporal_load(p) : *p;
         return uint4{v[0], v[1], v[2], v[3]};
     } else {
-        const u32x2 *p = reinterpret_cast<const u32x2 *>(wr) + c;
-        const u32x2 v = NT ? __builtin_nontemporal_load(p) : *p;
-        uint32_t lo = 0;
-        if constexpr (BITS == 3) {
-            const uint32_t *q = wr + 2 * C + c;
-            lo = NT ? __builtin_nontemporal_load(q) : *q;
+        if constexpr (BITS == 2) {
+            const u32x2 *p = reinterpret_cast<const u32x2 *>(wr) + c;
+            const u32x2 v = NT ? __builtin_nontemporal_load(p) : *p;
+            return uint4{v[0], v[1], 0u, 0u};
+        } else {
+            const uint32_t *q = wr + 3 * c;
+            if constexpr (NT)
+                return uint4{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                             __builtin_nontemporal_load(q + 2), 0u};
+            else
+                return uint4{q[0], q[1], q[2], 0u};
         }
-        return uint4{v[0], v[1], lo, 0u};
     }
 }
 
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
                 const int c = j + (k << log2g);
 #pragma unroll
                 for (int t = 0; t < ROWS; t++) {
-                    cw[t][k] = load_chunk<BITS, kValuNT>(wr[t], kc0 + c, Cf);
+                    cw[t][k] = load_chunk<BITS, kValuNT>(wr[t], kc0 + c);
                     if (sbl) continue;
 #if Q4MV_VALU_NT
                     // streamed once: non-temporal loads (no reuse to keep in the caches)
@@ -628,7 +632,7 @@ __global__ __launch_bounds__(kValuThreads, BITS == 4 ? 1 : Q4MV_LOWBIT_MIN_WAVES
                     for (int kk = 0; kk < 4; kk++) {
                         // clamped, unconditional loads (chunks past cpl are never used)
                         const int c = j + (min(k0 + kk, cpl - 1) << log2g);
-                        cc[t][kk] = load_chunk<BITS, false>(w_m + (size_t)rowc[t] * Cf * BITS, kc0 + c, Cf);
+                        cc[t][kk] = load_chunk<BITS, false>(w_m + (size_t)rowc[t] * Cf * BITS, kc0 + c);
                         sc[t][kk] = s_m[(size_t)rowc[t] * gf + g0 + (c >> 1)];
                         bc[t][kk] = b_m[(size_t)rowc[t] * gf + g0 + (c >> 1)];
                     }

@@ -208,11 +208,12 @@ int q4mv_swiglu_prep(const float *gu, int n_rows, int inter, void *xe, void *xo,
  * fn_q3_rows_h on the Constant BATCH_MSL page define them (codes q4 >> 2 and q4 >> 1). Each
  * 32-code chunk c of a row holds column t = 16i + 8u + p (i, u < 2, p < 8):
  *   Q2: q at bit 4p + 2u of word 2c + i (2 words per chunk);
- *   Q3: q >> 1 at that bit of word 2c + i, and q & 1 at bit 4p + 2i + u of word 2C + c,
- *       C = in_dim/32 (a row is its 2C upper-bit words, then its C lowest-bit words: the
- *       two planes of fn_q3_rows_h).
- * A row is C*bits words. (Every code sits in the nibble of its column within its 8-column
- * word, so one shift and one mask per word give the Q4 nibble layout.)
+ *   Q3: q >> 1 at that bit of word 3c + i, and q & 1 at bit 4p + 2i + u of word 3c + 2 (3
+ *       words per chunk: its two upper-bit words, then its lowest-bit word; the two planes
+ *       of fn_q3_rows_h, interleaved by chunk).
+ * A row is C*bits words, C = in_dim/32, and a chunk bits consecutive words. (Every code sits
+ * in the nibble of its column within its 8-column word, so one shift and one mask per word
+ * give the Q4 nibble layout.)
  *   codes : u8  [n_rows][in_dim]          one 4-bit code per byte (bits 4..7 ignored)
  *   w     : u32 [n_rows][in_dim/32*bits]  output (n_rows = n_mat * out_dim)
  * Errors: NULL pointer; bits not 2 or 3 (VALUE); n_rows < 1, in_dim < 64, in_dim % 64 != 0,

@@ -260,8 +260,8 @@ def pack_lowbit(bits, codes):
     """The packed low-bit words of 4-bit codes u8 [n_rows][in] -> u32 [n_rows][in/32*bits].
     Per 32-code chunk c, column t = 16i + 8u + p (i, u < 2, p < 8) holds q = q4 >> (4-bits):
     Q2: q at bit 4p + 2u of word 2c+i;
-    Q3: q >> 1 at that bit of word 2c+i, and q & 1 at bit 4p + 2i + u of word 2C+c (C = in/32:
-    the row's upper-bit words, then its lowest-bit words).
+    Q3: q >> 1 at that bit of word 3c+i, and q & 1 at bit 4p + 2i + u of word 3c+2 (a chunk
+    is its two upper-bit words, then its lowest-bit word).
     Column t's field sits in nibble p of the word that (shifted by 2u) lines up with the
     8 columns 16i + 8u + 0..7: one shift and one mask give a chunk's codes per nibble, and
     per f16 lane pair (p, p + 4) in place."""
@@ -281,7 +281,7 @@ def pack_lowbit(bits, codes):
             low |= (q[:, :, t] & 1) << (4 * p + 2 * i + u)
     if bits == 2:
         return up.reshape(n, 2 * C)
-    return np.concatenate([up.reshape(n, 2 * C), low], axis=1)
+    return np.concatenate([up, low[:, :, None]], axis=2).reshape(n, 3 * C)
 
 
 def _bf16_rne_bits(x):

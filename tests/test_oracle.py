@@ -571,9 +571,15 @@ def test_combine_closed_forms(oracle_lib):
 Q2_PROBES = [(0, 0, 0), (1, 0, 4), (3, 0, 12), (4, 0, 16), (7, 0, 28), (8, 0, 2), (11, 0, 14),
              (12, 0, 18), (15, 0, 30), (16, 1, 0), (20, 1, 16), (24, 1, 2), (31, 1, 30),
              (32, 2, 0), (45, 2, 22), (63, 3, 30)]
-# lowest-bit word of chunk c is word 2C + c (C = 2 here: words 4 and 5)
-Q3_LOW_PROBES = [(0, 4, 0), (4, 4, 16), (8, 4, 1), (13, 4, 21), (16, 4, 2), (20, 4, 18),
-                 (25, 4, 7), (31, 4, 31), (32, 5, 0), (63, 5, 31)]
+# Q3: chunk c is words 3c, 3c + 1 (the upper two bits, at the Q2 positions of words 2c,
+# 2c + 1) and its lowest-bit word 3c + 2 (words 2 and 5 here)
+Q3_LOW_PROBES = [(0, 2, 0), (4, 2, 16), (8, 2, 1), (13, 2, 21), (16, 2, 2), (20, 2, 18),
+                 (25, 2, 7), (31, 2, 31), (32, 5, 0), (63, 5, 31)]
+
+
+# the lowest-bit positions of the Q2 probe columns, from the same rule (4p + 2i + u)
+Q3_LOW_BIT = {0: 0, 1: 4, 3: 12, 4: 16, 7: 28, 8: 1, 11: 13, 12: 17, 15: 29, 16: 2, 20: 18,
+              24: 3, 31: 31, 32: 0, 45: 21, 63: 31}
 
 
 def test_lowbit_pack_probes(oracle_lib):
@@ -586,7 +592,11 @@ def test_lowbit_pack_probes(oracle_lib):
         # Q3: the upper two bits at the Q2 position, the lowest bit in the low-bit word
         codes[0, col] = 0b1110  # q3 = 7 -> upper 3, lowest 1
         w3 = oracle_lib.pack_lowbit(3, codes)[0]
-        assert w3[word] == np.uint32(3) << bit and w3[1 - word % 2 + 2 * (word // 2)] == 0
+        c, i = word // 2, word % 2
+        want = np.zeros(6, dtype=np.uint32)
+        want[3 * c + i] = np.uint32(3) << bit
+        want[3 * c + 2] = np.uint32(1) << Q3_LOW_BIT[col]
+        assert np.array_equal(w3, want), col
     for col, word, bit in Q3_LOW_PROBES:
         codes = np.zeros((1, 64), dtype=np.uint8)
         codes[0, col] = 0b0010  # q3 = 1: only the lowest bit
